@@ -1,0 +1,185 @@
+"""Seeded synthetic inputs: waveforms and random-init weights.
+
+This module is shared by the HIP path's tests and benchmark and by the
+oracle's tests. It holds no step of the encoder's arithmetic: it only draws
+random numbers (numpy ``default_rng``, PCG64) and shapes them into the
+workloads below. Every value is drawn in float64 and cast to float32; the
+bf16 variants round every matrix to the nearest bfloat16 (ties to even)
+before either side sees it, so both sides start from identical numbers.
+
+Workloads (16 kHz mono, t = n / 16000):
+
+* ``tone_clip``      one 1.0 s clip, 0.5*sin(2*pi*440 t) + N(0, 0.01^2), seed 0
+* ``multisine_clip`` 30 s: 8 sinusoids, f ~ U(50, 7900) Hz, a ~ U(0, 0.1),
+                     zero phase, + N(0, 0.02^2); one seed per clip
+* ``white_clip``     30 s of U(-1, 1), one seed per clip
+* ``ragged_batch``   64 clips, lengths ~ U{16000..480000} (seed 12345); clip i
+                     is N(0, 0.05^2) noise through the unity-DC-gain one-pole
+                     lowpass y[n] = 0.95 y[n-1] + 0.05 u[n]
+* ``make_weights``   matrices and conv kernels N(0, 1/fan_in); per_dim_scale
+                     N(0, 0.1) (0.1 read as the variance); norm gains
+                     1 + 0.1 N(0, 1); out_proj bias 0.1 N(0, 1); every
+                     clippable projection clamps at +-8.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+SR = 16000
+MAX_SAMPLES = 480000
+
+HIDDEN = 1024
+HEADS = 8
+HEAD_DIM = 128
+FF = 4096
+KERNEL = 5
+C0 = 128
+C1 = 32
+OUT_HIDDEN = 1536
+OUT_DIM = 512
+
+
+# ----------------------------------------------------------------- waveforms
+
+def tone_clip(seed: int = 0, n: int = 16000) -> np.ndarray:
+    rng = np.random.default_rng(seed)
+    t = np.arange(n, dtype=np.float64) / SR
+    x = 0.5 * np.sin(2 * np.pi * 440.0 * t) + rng.normal(0.0, 0.01, n)
+    return x.astype(np.float32)
+
+
+def multisine_clip(seed: int = 0, n: int = MAX_SAMPLES) -> np.ndarray:
+    rng = np.random.default_rng(seed)
+    f = rng.uniform(50.0, 7900.0, 8)
+    a = rng.uniform(0.0, 0.1, 8)
+    t = np.arange(n, dtype=np.float64) / SR
+    x = np.zeros(n, dtype=np.float64)
+    for fk, ak in zip(f, a):
+        x += ak * np.sin(2 * np.pi * fk * t)
+    x += rng.normal(0.0, 0.02, n)
+    return x.astype(np.float32)
+
+
+def white_clip(seed: int = 0, n: int = MAX_SAMPLES) -> np.ndarray:
+    return np.random.default_rng(seed).uniform(-1.0, 1.0, n).astype(np.float32)
+
+
+def ragged_lengths(count: int = 64, seed: int = 12345) -> np.ndarray:
+    return np.random.default_rng(seed).integers(16000, MAX_SAMPLES + 1, count)
+
+
+def pink_clip(seed: int, n: int) -> np.ndarray:
+    from scipy.signal import lfilter
+    u = np.random.default_rng(seed).normal(0.0, 0.05, n)
+    y = lfilter([0.05], [1.0, -0.95], u)
+    return y.astype(np.float32)
+
+
+def tone_batch():
+    """One 1 s tone clip (the smallest parity workload)."""
+    return [tone_clip(0)]
+
+
+def multisine_batch(clips: int, n: int = MAX_SAMPLES, first_seed: int = 0):
+    return [multisine_clip(first_seed + i, n) for i in range(clips)]
+
+
+def white_batch(clips: int, n: int = MAX_SAMPLES):
+    return [white_clip(i, n) for i in range(clips)]
+
+
+def ragged_batch(count: int = 64):
+    lens = ragged_lengths(count)
+    return [pink_clip(i, int(n)) for i, n in enumerate(lens)]
+
+
+def pack(clips):
+    """Concatenate clips back to back; returns (samples f32, offsets int64[B+1])."""
+    off = np.zeros(len(clips) + 1, dtype=np.int64)
+    for i, c in enumerate(clips):
+        off[i + 1] = off[i] + len(c)
+    wave = np.concatenate(clips).astype(np.float32) if clips else np.zeros(0, np.float32)
+    return wave, off
+
+
+# ------------------------------------------------------------------- weights
+
+def round_bf16(x: np.ndarray) -> np.ndarray:
+    """Nearest bfloat16 value (ties to even), returned as float32."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    lsb = (u >> 16) & 1
+    r = ((u + 0x7FFF + lsb) >> 16) << 16
+    return r.astype(np.uint32).view(np.float32).reshape(np.shape(x))
+
+
+def _mat(rng, out_f, in_f):
+    return (rng.standard_normal((out_f, in_f)) / np.sqrt(in_f)).astype(np.float32)
+
+
+def _gain(rng, n):
+    return (1.0 + 0.1 * rng.standard_normal(n)).astype(np.float32)
+
+
+CLIP8 = (-8.0, 8.0, -8.0, 8.0)
+
+# Names of every matrix a layer holds (rounded to bf16 in the bf16 workloads).
+LAYER_MATRICES = ("ff1_w1", "ff1_w2", "q", "k", "v", "post", "rel_k",
+                  "lc_start", "lc_end", "ff2_w1", "ff2_w2")
+TOP_MATRICES = ("conv1", "in_proj", "out_proj", "embed")
+
+
+def make_layer(seed: int, hidden: int = HIDDEN, heads: int = HEADS, ff: int = FF,
+               kernel: int = KERNEL, clip=CLIP8) -> dict:
+    rng = np.random.default_rng(seed)
+    hd = hidden // heads
+    L = {}
+    for f in ("ff1", "ff2"):
+        L[f + "_pre"] = _gain(rng, hidden)
+        L[f + "_w1"] = _mat(rng, ff, hidden)
+        L[f + "_w2"] = _mat(rng, hidden, ff)
+        L[f + "_post"] = _gain(rng, hidden)
+        L[f + "_w1_clip"] = clip
+        L[f + "_w2_clip"] = clip
+    L["attn_pre"] = _gain(rng, hidden)
+    for m in ("q", "k", "v", "post"):
+        L[m] = _mat(rng, hidden, hidden)
+        L[m + "_clip"] = clip
+    L["attn_post"] = _gain(rng, hidden)
+    L["per_dim_scale"] = rng.normal(0.0, np.sqrt(0.1), hd).astype(np.float32)
+    L["rel_k"] = _mat(rng, hidden, hidden)
+    L["lc_pre"] = _gain(rng, hidden)
+    L["lc_start"] = _mat(rng, 2 * hidden, hidden)
+    L["lc_start_clip"] = clip
+    L["lc_dw"] = (rng.standard_normal((hidden, kernel)) / np.sqrt(kernel)).astype(np.float32)
+    L["lc_norm"] = _gain(rng, hidden)
+    L["lc_end"] = _mat(rng, hidden, hidden)
+    L["lc_end_clip"] = clip
+    L["norm_out"] = _gain(rng, hidden)
+    return L
+
+
+def make_weights(layers: int = 12, bf16: bool = False, clip=CLIP8) -> dict:
+    """The whole encoder's parameters. Seeds: 999 for the subsampler and the
+    head, 1000 + i for layer i."""
+    rng = np.random.default_rng(999)
+    W = {}
+    W["conv0"] = (rng.standard_normal((C0, 1, 3, 3)) / np.sqrt(9.0)).astype(np.float32)
+    W["ln0"] = _gain(rng, C0)
+    W["conv1"] = (rng.standard_normal((C1, C0, 3, 3)) / np.sqrt(C0 * 9.0)).astype(np.float32)
+    W["ln1"] = _gain(rng, C1)
+    W["in_proj"] = _mat(rng, HIDDEN, C1 * 32)
+    W["out_proj"] = _mat(rng, OUT_HIDDEN, HIDDEN)
+    W["out_bias"] = (0.1 * rng.standard_normal(OUT_HIDDEN)).astype(np.float32)
+    W["embed"] = _mat(rng, OUT_DIM, OUT_HIDDEN)
+    W["layers"] = [make_layer(1000 + i, clip=clip) for i in range(layers)]
+    if bf16:
+        for k in TOP_MATRICES:
+            W[k] = round_bf16(W[k])
+        for L in W["layers"]:
+            for k in LAYER_MATRICES:
+                L[k] = round_bf16(L[k])
+    return W
+
+
+CONFIG = dict(hidden=HIDDEN, heads=HEADS, left=12, n_dist=13, kernel=KERNEL,
+              softcap=50.0, residual_weight=0.5, eps=1e-6)
