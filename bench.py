@@ -1,0 +1,174 @@
+"""Throughput of the audio-encoder forward on one MI355X.
+
+Default workload: 32 clips x 30 s (multisine + noise, seeds 0..31), the
+whole encoder (log-mel, subsampler, 12 Conformer layers, head) with bf16
+weights and projection operands on MFMA, fp32 accumulation, norms and
+residual stream; random-init weights. A step is one ae_encode over the
+batch, inputs already resident in HBM. Prints one JSON line.
+
+  python bench.py [--gpus 1] [--steps 20] [--warmup 5]
+                  [--workload batch32|frontend256|ragged64]
+                  [--kernel gemm_ffn1] [--no-cpu-baseline]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "audio-seconds encoded/sec (log-mel + 12-layer Conformer, batch 32); % roofline"
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_F32_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def gemm_flops_per_launch(cls, tokens, cfg):
+    d, ff = cfg.hidden, cfg.ff
+    return {
+        "gemm_ffn1": 2.0 * tokens * ff * d,
+        "gemm_ffn2": 2.0 * tokens * d * ff,
+        "gemm_qkv": 2.0 * tokens * 3 * d * d,
+        "gemm_post": 2.0 * tokens * d * d,
+        "gemm_lcstart": 2.0 * tokens * 2 * d * d,
+        "gemm_lcend": 2.0 * tokens * d * d,
+    }[cls]
+
+
+def cpu_baseline(clip, W, seconds):
+    """The oracle (f64 numpy) on one clip of the workload, timed on the host."""
+    import oracle
+    from threadpoolctl import threadpool_info
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    t0 = time.perf_counter()
+    oracle.encode_clips([clip], W)
+    dt = time.perf_counter() - t0
+    return {"value": seconds / dt, "unit": "audio-s/s", "cores": threads, "kind": "oracle",
+            "sample": f"1 clip of the workload ({seconds:.0f} s, {len(clip)} samples), full "
+                      f"encoder in float64 numpy, {dt:.1f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="batch32", choices=["batch32", "frontend256", "ragged64"])
+    ap.add_argument("--kernel", default="gemm_ffn1")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for {args.gpus}); "
+              "clips are independent, so more GPUs would each encode their own share.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from log_mel_conformer_amd import ae, synth
+
+    torch.cuda.set_device(0)
+    log(f"[bench] workload {args.workload}: generating inputs")
+    if args.workload == "batch32":
+        clips = synth.multisine_batch(32)
+    elif args.workload == "ragged64":
+        clips = synth.ragged_batch(64)
+    else:
+        clips = synth.white_batch(256)
+    wave_np, so = synth.pack(clips)
+    wave = torch.from_numpy(wave_np).cuda()
+    pl = ae.plan(np.diff(so))
+    audio_s = float(pl["sample_off"][-1]) / 16000.0
+    tokens = int(pl["token_off"][-1])
+    frames = int(pl["frame_off"][-1])
+
+    W = None
+    if args.workload == "frontend256":
+        mel = torch.empty((frames, 128), dtype=torch.float32, device="cuda")
+        step = lambda: ae.logmel(wave, so, out=mel)  # noqa: E731
+        kclass = "logmel"
+        dtype = "f32"
+    else:
+        log("[bench] generating weights (12 layers, bf16)")
+        W = synth.make_weights(layers=12, bf16=True)
+        model = ae.Model(W, dtype="bf16")
+        out = torch.empty((tokens, 512), dtype=torch.float32, device="cuda")
+        model.workspace(len(clips), frames, tokens)
+        step = lambda: ae.encode(model, wave, so, out=out)  # noqa: E731
+        kclass = args.kernel
+        dtype = "bf16"
+
+    log(f"[bench] warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"[bench] timing {args.steps} steps (events around {kclass})")
+    ae.timing_enable(kclass)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    launches, kms = ae.timing_read()
+    ae.timing_enable(None)
+    ms = (t1 - t0) * 1e3 / args.steps
+    value = audio_s / (ms / 1e3)
+    avg_ms = kms / max(launches, 1)
+
+    if kclass == "logmel":
+        # algorithmic bytes: every input sample read once, every log-mel value written once
+        per_launch = 4.0 * float(pl["sample_off"][-1]) + 4.0 * 128 * frames
+        achieved = per_launch / (avg_ms / 1e3) / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": achieved / PEAK_HBM_GBS, "traffic": None, "kernel": "k_logmel",
+                "avg_ms": avg_ms, "launches": launches}
+    else:
+        flops = gemm_flops_per_launch(kclass, tokens, model.cfg)
+        achieved = flops / (avg_ms / 1e3) / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+                "kernel": kclass, "avg_ms": avg_ms, "launches": launches}
+
+    cpu = None
+    if not args.no_cpu_baseline and W is not None:
+        log("[bench] cpu baseline: oracle on one clip")
+        cpu = cpu_baseline(clips[0], W, len(clips[0]) / 16000.0)
+    elif not args.no_cpu_baseline:
+        import oracle
+        from threadpoolctl import threadpool_info
+        t0 = time.perf_counter()
+        n = 0
+        while time.perf_counter() - t0 < 10.0 and n < len(clips):
+            oracle.log_mel(clips[n])
+            n += 1
+        dt = time.perf_counter() - t0
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        cpu = {"value": n * 30.0 / dt, "unit": "audio-s/s", "cores": threads, "kind": "oracle",
+               "sample": f"log-mel of {n} of the 256 clips in float64 numpy"}
+
+    names = {"batch32": "32 clips x 30 s multisine+noise: log-mel, subsampler, 12 Conformer "
+                        "layers, head (bf16 MFMA, fp32 accumulation and norms)",
+             "ragged64": "64 clips, 1-30 s pink noise, packed ragged: full encoder, bf16",
+             "frontend256": "256 clips x 30 s white noise: log-mel front end only, fp32"}
+    rec = {"metric": METRIC, "value": value, "unit": "audio-s/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dtype,
+           "data": "synthetic (seeded waveforms, random-init weights)",
+           "config": {"workload": names[args.workload], "global_batch": len(clips),
+                      "seq_len": int(max(np.diff(pl["token_off"]))) if tokens else 0,
+                      "tokens": tokens, "frames": frames, "audio_seconds": audio_s,
+                      "tokens_per_s": tokens / (ms / 1e3), "parallelism": "none (1 GPU)"},
+           "roofline": roof, "cpu_baseline": cpu}
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,216 @@
+/*
+ * ae.h -- C ABI of libae.so: the forward pass of the log-mel + Conformer
+ * audio encoder (the gemma4_audio tower of EmbeddingGemma 2) on MI355X
+ * (gfx950), in hand-written HIP kernels.
+ *
+ * The operations follow the docs.rs source page of cortiq-engine 0.8.49,
+ * cortiq_engine/egemma2_audio.rs ("the page" below): its module
+ * documentation (steps 1-5), MelFrontend::log_mel, AudioTower::subsample,
+ * ffn, attention, dwconv, glu, norm_silu and encode_locked.
+ *
+ * Conventions, for every entry point:
+ *  - Data pointers marked "device" are device memory on the current HIP
+ *    device, owned by the caller; they must stay valid until the work
+ *    queued on `stream` has finished. Pointers marked "host" are read
+ *    before the call returns.
+ *  - Row-major layouts, rows = frames or tokens, packed clip after clip.
+ *  - Every compute call is asynchronous on `stream` (0 = the null stream)
+ *    and allocates no device memory; it validates its arguments first and
+ *    returns an error before queuing any work.
+ *  - Errors: a non-zero ae_status; ae_last_error() then returns a message
+ *    for the calling thread. A failed launch reports AE_ERR_HIP.
+ *  - A clip of <= 160 samples has 0 frames and 0 tokens (not an error);
+ *    samples past 480000 (30 s at 16 kHz) are ignored.
+ *  - Calls that share a workspace must not overlap in time.
+ */
+#ifndef AE_H
+#define AE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* ae_stream; /* a hipStream_t */
+
+typedef enum {
+  AE_OK = 0,
+  AE_ERR_INVALID = 1,     /* null pointer, negative size, bad layer index */
+  AE_ERR_SHAPE = 2,       /* a weight or size does not fit the configuration */
+  AE_ERR_CAPACITY = 3,    /* workspace too small, or an index beyond int32 */
+  AE_ERR_UNSUPPORTED = 4, /* a configuration this build does not implement */
+  AE_ERR_HIP = 5          /* a HIP runtime call failed */
+} ae_status;
+
+/* Arithmetic of the tower. AE_F32: fp32 everywhere (fp32 MFMA for the
+ * projections). AE_BF16: bf16 matrices and bf16 projection operands on
+ * bf16 MFMA, fp32 accumulation, fp32 residual stream, norms, softmax. */
+typedef enum { AE_F32 = 0, AE_BF16 = 1 } ae_dtype;
+
+/* Tower hyper-parameters (the page: AudioTower::load and its defaults). */
+typedef struct {
+  int32_t hidden;          /* 1024 */
+  int32_t heads;           /* 8 (head_dim = hidden / heads = 128) */
+  int32_t layers;          /* 12 */
+  int32_t ff;              /* 4096, width of the feed-forward */
+  int32_t conv_kernel;     /* 5, light-conv depthwise taps */
+  int32_t chunk;           /* 12, attention_chunk_size */
+  int32_t ctx_left;        /* 13; a token sees ctx_left - 1 = 12 keys */
+  int32_t ctx_right;       /* 0; any other value is AE_ERR_UNSUPPORTED */
+  float softcap;           /* 50, tanh logit cap */
+  float residual_weight;   /* 0.5, feed-forward residual scale */
+  int32_t out_hidden;      /* 1536, output_proj width */
+  int32_t out_dim;         /* 512, embed_audio width */
+} ae_config;
+
+/* Bounds of a clippable projection: the input is clamped to
+ * [in_lo, in_hi] before the product and the output to [out_lo, out_hi]
+ * after it (the page: ClipLin). +-INFINITY disables a bound. */
+typedef struct { float in_lo, in_hi, out_lo, out_hi; } ae_clip;
+
+/* One Conformer layer. Matrices ("mat") are [out][in] row-major in the
+ * model's dtype (float or bf16); vectors are float. All device pointers,
+ * borrowed: they must outlive the model. y = x W^T throughout. */
+typedef struct {
+  const float* ff1_pre;  const void* ff1_w1; ae_clip ff1_w1_clip;  /* [ff][hidden] */
+  const void* ff1_w2;    ae_clip ff1_w2_clip; const float* ff1_post; /* [hidden][ff] */
+  const float* attn_pre;
+  const void* q; ae_clip q_clip;          /* [hidden][hidden] each */
+  const void* k; ae_clip k_clip;
+  const void* v; ae_clip v_clip;
+  const void* post; ae_clip post_clip;
+  const float* attn_post;
+  const float* per_dim_scale;             /* [head_dim] */
+  const void* rel_k;                      /* relative_k_proj [hidden][hidden], no clamp */
+  const float* lc_pre;
+  const void* lc_start; ae_clip lc_start_clip;  /* [2*hidden][hidden] */
+  const float* lc_dw;                     /* [hidden][conv_kernel] */
+  const float* lc_norm;
+  const void* lc_end; ae_clip lc_end_clip;      /* [hidden][hidden] */
+  const float* ff2_pre;  const void* ff2_w1; ae_clip ff2_w1_clip;
+  const void* ff2_w2;    ae_clip ff2_w2_clip; const float* ff2_post;
+  const float* norm_out;
+} ae_layer_weights;
+
+/* The whole encoder (device pointers except `layers`, a host array of
+ * cfg.layers entries read during ae_model_create). */
+typedef struct {
+  const float* conv0;      /* [128][1][3][3] */
+  const float* ln0;        /* [128] LayerNorm gain */
+  const void* conv1;       /* [32][128][3][3], model dtype */
+  const float* ln1;        /* [32] */
+  const void* in_proj;     /* [hidden][1024], model dtype, no clamp */
+  const ae_layer_weights* layers;
+  const void* out_proj;    /* [out_hidden][hidden], model dtype */
+  const float* out_bias;   /* [out_hidden] */
+  const void* embed;       /* [out_dim][out_hidden], model dtype */
+} ae_weights;
+
+typedef struct ae_model ae_model; /* opaque */
+
+/* Fill `cfg` with the release's defaults listed in ae_config. */
+void ae_config_default(ae_config* cfg);
+
+/* Message of the last error on this thread ("" if none). */
+const char* ae_last_error(void);
+
+/* --- sizes (host only; the page: num_frames, num_tokens) ------------- */
+
+/* Log-mel frames of an n-sample clip: 0 if n <= 160, else
+ * ceil((n - 160) / 160), after capping n at 480000. */
+int64_t ae_num_frames(int64_t n_samples);
+/* Soft tokens: ceil(ceil(frames / 2) / 2). */
+int64_t ae_num_tokens(int64_t n_samples);
+
+/* Prefix sums of a batch of B clips of n_samples[i] samples (host arrays,
+ * each of B + 1 entries written by the call, entry 0 = 0): samples (capped
+ * at 480000 per clip), frames, conv0 rows (ceil(frames / 2)) and tokens.
+ * Any output may be NULL. Negative lengths are AE_ERR_INVALID. */
+ae_status ae_plan(const int64_t* n_samples, int32_t B, int64_t* sample_off,
+                  int64_t* frame_off, int64_t* row_off, int64_t* token_off);
+
+/* --- model ----------------------------------------------------------- */
+
+/* Validate the configuration and weights and build the derived tables
+ * (relative keys R = PE rel_k^T per layer, softplus(per_dim_scale) folded
+ * into the query scale, conv1 weights reordered for the implicit GEMM).
+ * Allocates those tables (a few MB) on the current device; work is queued
+ * on `stream` and finished before return. On error *out is NULL. */
+ae_status ae_model_create(const ae_config* cfg, const ae_weights* w, ae_dtype dtype,
+                          ae_stream stream, ae_model** out);
+void ae_model_destroy(ae_model* m);
+
+/* Workspace bytes needed by ae_subsample / ae_conformer_layer / ae_encode
+ * for a batch of B clips with these totals (frames, tokens over the batch). */
+size_t ae_workspace_bytes(const ae_model* m, int32_t B, int64_t total_frames,
+                          int64_t total_tokens);
+/* Workspace bytes needed by ae_logmel for B clips. */
+size_t ae_logmel_workspace_bytes(int32_t B);
+
+/* --- compute --------------------------------------------------------- */
+
+/* Log-mel features (the page: module documentation step 2 and
+ * MelFrontend::log_mel). wave: device float, the B clips back to back,
+ * clip i at [sample_off[i], sample_off[i+1]) (host int64 [B+1],
+ * non-decreasing, sample_off[0] = 0). mel: device float [sum F_i][128],
+ * clip after clip, F_i = ae_num_frames(length i). Frame j of a clip is
+ * the 320 samples starting 160 (j - 1) (zeros before the clip start),
+ * times the periodic Hann window, zero-padded to 512, |rFFT| on 257 bins,
+ * 128 HTK mel bands over 0..8 kHz, ln(band + 0.001). */
+ae_status ae_logmel(const float* wave, const int64_t* sample_off, int32_t B, float* mel,
+                    void* ws, size_t ws_bytes, ae_stream stream);
+
+/* Subsampler and input projection (the page: step 3, AudioTower::subsample
+ * and input_proj_linear). mel: device float [sum F_i][128] with clip i at
+ * rows [frame_off[i], frame_off[i+1]) (host int64 [B+1]). x: device float
+ * [sum T_i][hidden], T_i = ceil(F_i / 4). */
+ae_status ae_subsample(const ae_model* m, const float* mel, const int64_t* frame_off,
+                       int32_t B, float* x, void* ws, size_t ws_bytes, ae_stream stream);
+
+/* One Conformer layer in place (the page: step 4, encode_locked's loop
+ * body): FFN1, local attention, light conv, FFN2, RMS norm_out.
+ * h: device float [n][hidden]; pos: device int32 [n], each row's index
+ * inside its clip (rows of one clip are consecutive, pos 0, 1, 2, ...).
+ * The workspace must hold ae_workspace_bytes(m, 1, 0, n). */
+ae_status ae_conformer_layer(const ae_model* m, int32_t layer, float* h, const int32_t* pos,
+                             int64_t n, void* ws, size_t ws_bytes, ae_stream stream);
+
+/* The whole encoder (the page: soft_tokens / encode_locked): log-mel,
+ * subsampler, all layers, then output_proj + bias, a weightless RMS norm
+ * and embed_audio. out: device float [sum T_i][out_dim], clip after clip.
+ * trace (nullable, host array of cfg.layers + 2 device float pointers, each
+ * entry nullable): [0] receives the subsampler output [sum T][hidden],
+ * [1 + l] layer l's output [sum T][hidden], [layers + 1] the output
+ * projection plus bias [sum T][out_hidden]. */
+ae_status ae_encode(const ae_model* m, const float* wave, const int64_t* sample_off,
+                    int32_t B, float* out, float* const* trace, void* ws, size_t ws_bytes,
+                    ae_stream stream);
+
+/* --- measurement ----------------------------------------------------- */
+
+/* Kernel classes the library can time with HIP events recorded on the
+ * stream each launch goes to. AE_K_GEMM_FFN1 is the feed-forward's first
+ * (widening) projection, AE_K_GEMM_FFN2 its second; AE_K_GEMM_HEAD covers
+ * input_proj, output_proj and embed_audio. */
+typedef enum {
+  AE_K_LOGMEL = 0, AE_K_CONV0 = 1, AE_K_CONV1 = 2, AE_K_GEMM_FFN1 = 3,
+  AE_K_GEMM_FFN2 = 4, AE_K_GEMM_QKV = 5, AE_K_GEMM_POST = 6, AE_K_GEMM_LCSTART = 7,
+  AE_K_GEMM_LCEND = 8, AE_K_GEMM_HEAD = 9, AE_K_ROWNORM = 10, AE_K_ATTN = 11,
+  AE_K_LCONV = 12, AE_K_COUNT = 13
+} ae_kernel_class;
+
+/* Process-wide: from now on, bracket every launch of kernel class `cls`
+ * with a pair of HIP events (up to 4096 launches are kept until read);
+ * cls = -1 turns timing off. Not for concurrent use from several threads.
+ * Unknown classes are AE_ERR_INVALID. */
+ae_status ae_timing_enable(int32_t cls);
+/* Wait for the recorded events, return the number of timed launches and
+ * their summed duration in milliseconds, and clear the record. */
+ae_status ae_timing_read(int64_t* launches, double* total_ms);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* AE_H */

@@ -1,0 +1,77 @@
+// Internal definitions shared by the HIP sources of libae.so (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <string>
+
+#include "../../include/ae.h"
+
+namespace ae {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kSampleRate = 16000;
+constexpr int kMaxSamples = 480000;
+constexpr int kFrame = 320;
+constexpr int kHop = 160;
+constexpr int kFft = 512;
+constexpr int kBins = kFft / 2 + 1;  // 257
+constexpr int kMels = 128;
+constexpr float kMelFloor = 1e-3f;
+constexpr float kEps = 1e-6f;
+constexpr int kC0 = 128;   // conv0 channels
+constexpr int kC1 = 32;    // conv1 channels
+constexpr int kF1 = 64;    // frequencies after conv0
+constexpr int kF2 = 32;    // frequencies after conv1
+
+// Error reporting: a thread-local message returned by ae_last_error().
+ae_status set_error(ae_status s, const std::string& msg);
+
+#define AE_HIP_TRY(expr)                                                        \
+  do {                                                                          \
+    hipError_t e_ = (expr);                                                     \
+    if (e_ != hipSuccess)                                                       \
+      return ::ae::set_error(AE_ERR_HIP, std::string(#expr) + ": " +          \
+                                             hipGetErrorString(e_));            \
+  } while (0)
+
+// Launch bookkeeping: a kernel launch followed by the error check, with
+// optional HIP-event timing for one kernel class.
+void timing_begin(int cls, hipStream_t s);
+void timing_end(int cls, hipStream_t s);
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }
+
+__device__ __forceinline__ float clampf(float x, float lo, float hi) {
+  return fminf(fmaxf(x, lo), hi);
+}
+__device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + __expf(-x)); }
+
+// Sum over the 64 lanes of a wavefront; every lane gets the total.
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// Index of the clip holding packed row `r`: the largest c with off[c] <= r,
+// for a non-decreasing off[0..B] (binary search).
+__device__ __forceinline__ int find_clip(const int64_t* off, int B, int64_t r) {
+  int lo = 0, hi = B - 1;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (off[mid] <= r) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+}  // namespace ae

@@ -1,0 +1,110 @@
+// Internal launchers: one per kernel family. Each returns hipSuccess or the
+// launch error; shapes are validated by the caller (the C-ABI layer).
+#pragma once
+
+#include "common.h"
+
+namespace ae {
+
+// ----------------------------------------------------------------- GEMM
+// C = epilogue(A B^T): A [M][K], B [N][K] row-major, fp32 accumulation.
+enum EpiKind {
+  EPI_STORE = 0,   // C = clamp(acc, olo, ohi) * colscale[col]       (TO)
+  EPI_SILU = 1,    // C = clamp(silu(clamp(acc, olo, ohi)), nlo, nhi) (TO)
+  EPI_GLU = 2,     // C[:, j] = a * sigmoid(b), a/b the clamped halves (TO)
+  EPI_RESID = 3,   // C (float) += clamp(acc, olo, ohi)
+  EPI_BIAS = 4,    // C (float) = acc + bias[col]
+  EPI_LNRELU = 5   // C = relu(LayerNorm_32(acc) * gain)  (conv1, N = 32)
+};
+enum ALoadKind { A_PLAIN = 0, A_CONV1 = 1 };
+
+struct GemmParams {
+  int M, N, K;
+  // A: plain row-major, one pointer per B segment (qkv may clamp apart)
+  const void* A[3];
+  int lda;
+  // A_CONV1: implicit im2col over conv0 rows y0 [rows][64][128]
+  const void* y0;
+  const int64_t* row_off;   // conv0 row offsets per clip [B+1]
+  const int32_t* tok_pos;   // token -> index in clip
+  const int32_t* tok_clip;  // token -> clip
+  int n_tok;
+  // B: up to 3 row segments of seg_n rows (N = sum), leading dim ldb
+  const void* Bm[3];
+  int seg_n, ldb;
+  int glu_d;                // EPI_GLU: output width; B rows [0,d) = a, [d,2d) = b
+  // epilogue
+  void* C;
+  int ldc;
+  float olo[3], ohi[3];
+  float nlo, nhi;
+  const float* colscale;
+  const float* bias;
+  const float* gain;
+};
+
+// dtype: AE_F32 or AE_BF16 operands; out_bf16: TO = bf16 (else float).
+hipError_t launch_gemm(ae_dtype dt, int epi, int aload, bool out_bf16, const GemmParams& p,
+                       hipStream_t s);
+
+// -------------------------------------------------------------- front end
+hipError_t mel_tables_init();
+hipError_t launch_logmel(const float* wave, const int64_t* sample_off, const int64_t* frame_off,
+                         int B, int64_t total_frames, float* mel, hipStream_t s);
+
+// --------------------------------------------------------------- conv0
+hipError_t launch_conv0(ae_dtype dt, const float* mel, const int64_t* frame_off,
+                        const int64_t* row_off, int B, int64_t total_rows, const float* w0,
+                        const float* g0, void* y0, hipStream_t s);
+
+// -------------------------------------------------------------- row norms
+// For each row of h [n][d]:
+//   if y:     h += scale * rms(y) * w_post
+//   if w_out: h  = rms(h) * w_out
+//   store h (when y or w_out was applied)
+//   if w_next: a_i = clamp(rms(h) * w_next, lo_i, hi_i) for i < n_out (dtype dt)
+// With w_next = nullptr and h_in_place false, nothing but the a_i are written.
+struct RowNormParams {
+  int64_t n;
+  int d;
+  float* h;
+  const float* y;
+  float scale;
+  const float* w_post;
+  const float* w_out;
+  const float* w_next;   // may be null: then a weightless norm if out_plain
+  bool plain_next;       // weightless rms for a_i (head)
+  void* a[3];
+  float lo[3], hi[3];
+  int n_out;
+};
+hipError_t launch_rownorm(ae_dtype dt, const RowNormParams& p, hipStream_t s);
+
+// ------------------------------------------------------------- attention
+// qkv [n][3d] (dtype dt; q, k already scaled), R [left][d] float,
+// pos [n] -> o [n][d] (dtype dt) clamped to [lo, hi].
+hipError_t launch_attention(ae_dtype dt, const void* qkv, const float* R, const int32_t* pos,
+                            int64_t n, int d, int heads, int left, float softcap, float lo,
+                            float hi, void* o, hipStream_t s);
+
+// ------------------------------------------------------------ light conv
+// u [n][d] (dt) -> c = clamp(silu(rms(dwconv(u)) * w_norm), lo, hi) (dt)
+hipError_t launch_lconv(ae_dtype dt, const void* u, const float* w_dw, int kernel,
+                        const float* w_norm, const int32_t* pos, int64_t n, int d, float lo,
+                        float hi, void* c, hipStream_t s);
+
+// ---------------------------------------------------------- bookkeeping
+// Write the packed-offset table (host values passed by value) to `dst`.
+hipError_t launch_write_i64(int64_t* dst, const int64_t* host_vals, int count, hipStream_t s);
+// tok_pos / tok_clip from token_off [B+1] (device).
+hipError_t launch_token_index(const int64_t* token_off, int B, int64_t n_tok, int32_t* tok_pos,
+                              int32_t* tok_clip, hipStream_t s);
+// Model tables: R = PE rel_k^T ([n_dist][d] float), colscale for q|k|v,
+// conv1 weights reordered to [32][(dt*3+df)*128 + ci].
+hipError_t launch_relative_keys(ae_dtype dt, const void* rel_k, int d, int n_dist, float* R,
+                                hipStream_t s);
+hipError_t launch_qkv_scale(const float* pds, int d, int head_dim, float q_scale, float k_scale,
+                            float* colscale, hipStream_t s);
+hipError_t launch_conv1_reorder(ae_dtype dt, const void* w1, void* w1r, hipStream_t s);
+
+}  // namespace ae

@@ -1,0 +1,114 @@
+// Fused row kernels around the residual stream: the RMS norms of the tower
+// (x / sqrt(mean(x^2) + 1e-6) times the weight plainly; ltxdit.rs rms_w /
+// rms_plain, egemma2_audio.rs module documentation step 4) and the
+// residual updates that surround them (egemma2_audio.rs add_normed, ffn,
+// encode_locked).
+//
+// One wavefront per row; a lane holds VPL = d/64 values, loaded as float4
+// so that every load instruction of the wavefront covers 1 KB of
+// contiguous memory. A row is read once and every norm of the chain
+// (post-norm residual, norm_out, the next block's pre-norm and the next
+// projection's input clamp) is applied while it sits in registers.
+#include "launch.h"
+
+namespace ae {
+namespace {
+
+template <typename T, int VPL>
+__global__ void __launch_bounds__(256) k_rownorm(RowNormParams p) {
+  constexpr int NV = VPL / 4;
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= p.n) return;  // uniform per wavefront
+  const int d = p.d;
+  const float invd = 1.0f / (float)d;
+  float x[VPL];
+  float* hrow = p.h + row * d;
+#pragma unroll
+  for (int q = 0; q < NV; ++q) {
+    const float4 v = *(const float4*)(hrow + q * 256 + lane * 4);
+    x[4 * q] = v.x; x[4 * q + 1] = v.y; x[4 * q + 2] = v.z; x[4 * q + 3] = v.w;
+  }
+  if (p.y) {
+    float y[VPL];
+    const float* yrow = p.y + row * d;
+    float ss = 0.f;
+#pragma unroll
+    for (int q = 0; q < NV; ++q) {
+      const float4 v = *(const float4*)(yrow + q * 256 + lane * 4);
+      y[4 * q] = v.x; y[4 * q + 1] = v.y; y[4 * q + 2] = v.z; y[4 * q + 3] = v.w;
+    }
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) ss += y[i] * y[i];
+    const float inv = rsqrtf(wave_sum(ss) * invd + kEps);
+#pragma unroll
+    for (int q = 0; q < NV; ++q)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int c = q * 256 + lane * 4 + e;
+        x[4 * q + e] += p.scale * (y[4 * q + e] * inv * p.w_post[c]);
+      }
+  }
+  if (p.w_out) {
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) ss += x[i] * x[i];
+    const float inv = rsqrtf(wave_sum(ss) * invd + kEps);
+#pragma unroll
+    for (int q = 0; q < NV; ++q)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int c = q * 256 + lane * 4 + e;
+        x[4 * q + e] = x[4 * q + e] * inv * p.w_out[c];
+      }
+  }
+  if (p.y || p.w_out) {
+#pragma unroll
+    for (int q = 0; q < NV; ++q)
+      *(float4*)(hrow + q * 256 + lane * 4) =
+          make_float4(x[4 * q], x[4 * q + 1], x[4 * q + 2], x[4 * q + 3]);
+  }
+  if (p.w_next || p.plain_next) {
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) ss += x[i] * x[i];
+    const float inv = rsqrtf(wave_sum(ss) * invd + kEps);
+#pragma unroll
+    for (int q = 0; q < NV; ++q)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int c = q * 256 + lane * 4 + e;
+        x[4 * q + e] = x[4 * q + e] * inv * (p.w_next ? p.w_next[c] : 1.0f);
+      }
+    for (int s = 0; s < p.n_out; ++s) {
+      T* arow = (T*)p.a[s] + row * d;
+      const float lo = p.lo[s], hi = p.hi[s];
+#pragma unroll
+      for (int q = 0; q < NV; ++q)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          arow[q * 256 + lane * 4 + e] = from_f32<T>(clampf(x[4 * q + e], lo, hi));
+    }
+  }
+}
+
+template <typename T>
+hipError_t run(const RowNormParams& p, hipStream_t s) {
+  const unsigned grid = (unsigned)((p.n + 3) / 4);
+  switch (p.d) {
+    case 1024: hipLaunchKernelGGL((k_rownorm<T, 16>), dim3(grid), dim3(256), 0, s, p); break;
+    case 1536: hipLaunchKernelGGL((k_rownorm<T, 24>), dim3(grid), dim3(256), 0, s, p); break;
+    case 2048: hipLaunchKernelGGL((k_rownorm<T, 32>), dim3(grid), dim3(256), 0, s, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_rownorm(ae_dtype dt, const RowNormParams& p, hipStream_t s) {
+  if (p.n <= 0) return hipSuccess;
+  return dt == AE_BF16 ? run<bf16>(p, s) : run<float>(p, s);
+}
+
+}  // namespace ae

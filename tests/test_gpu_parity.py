@@ -1,0 +1,294 @@
+"""GPU parity: the HIP path (through the C ABI) against the oracle.
+
+Tolerances: log-mel elementwise |d| <= 1e-4 * max(1, |o|); every fp32
+stage ||g - o||_2 / ||o||_2 <= 1e-4 per clip; bf16 final embeddings
+<= 2e-2 per clip. Integer quantities (frame and token counts) are exact.
+Full-size workloads compare sampled clips (clips are independent, so the
+oracle runs those clips alone).
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from log_mel_conformer_amd import synth
+from _util import rel_l2, rel_max, say, weights
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # pragma: no cover
+    pytest.skip("no GPU", allow_module_level=True)
+
+from log_mel_conformer_amd import ae  # noqa: E402
+
+FP32_TOL = 1e-4
+BF16_TOL = 2e-2
+
+
+def cuda(x, dtype=torch.float32):
+    return torch.as_tensor(np.asarray(x)).to("cuda", dtype)
+
+
+def logmel_ok(g, o):
+    g = np.asarray(g, np.float64)
+    o = np.asarray(o, np.float64)
+    assert g.shape == o.shape
+    bound = 1e-4 * np.maximum(1.0, np.abs(o))
+    bad = np.abs(g - o) > bound
+    assert not bad.any(), f"{bad.sum()} log-mel values off, worst {np.max(np.abs(g - o))}"
+
+
+# ------------------------------------------------------------------ log-mel
+
+def test_logmel_tone_clip():
+    say("[gpu] logmel: 1 s tone, seed 0")
+    x = synth.tone_clip(0)
+    wave, so = synth.pack([x])
+    g = ae.logmel(cuda(wave), so).cpu().numpy()
+    assert g.shape == (99, 128)
+    logmel_ok(g, oracle.log_mel(x))
+
+
+def test_logmel_ragged_batch_and_edges():
+    say("[gpu] logmel: ragged batch with odd offsets, tiny and over-long clips")
+    rng = np.random.default_rng(5)
+    clips = [rng.uniform(-1, 1, n).astype(np.float32)
+             for n in (161, 100, 321, 481, 1001, 160, 4000, 3)]
+    clips.append(synth.white_clip(9, 480000 + 777))   # truncated at 30 s
+    wave, so = synth.pack(clips)
+    g = ae.logmel(cuda(wave), so).cpu().numpy()
+    F = [oracle.num_frames(len(c)) for c in clips]
+    assert g.shape[0] == sum(F)
+    off = 0
+    for c, f in zip(clips, F):
+        if f:
+            logmel_ok(g[off:off + f], oracle.log_mel(c))
+        off += f
+
+
+def test_logmel_silence_and_impulse():
+    say("[gpu] logmel: silence and impulse")
+    z = np.zeros(16000, np.float32)
+    imp = np.zeros(1000, np.float32)
+    imp[80] = 1.0
+    wave, so = synth.pack([z, imp])
+    g = ae.logmel(cuda(wave), so).cpu().numpy()
+    assert np.all(np.abs(g[:99] - math.log(1e-3)) < 1e-6)
+    logmel_ok(g[99:], oracle.log_mel(imp))
+
+
+def test_logmel_full_batch_sampled():
+    """256 clips x 30 s of white noise; sampled clips checked in full."""
+    say("[gpu] logmel: 256 x 30 s white noise (full size), sampled clips")
+    clips = synth.white_batch(256)
+    wave, so = synth.pack(clips)
+    g = ae.logmel(cuda(wave), so).cpu().numpy()
+    assert g.shape == (256 * 2999, 128)
+    for i in (0, 137, 255):
+        logmel_ok(g[i * 2999:(i + 1) * 2999], oracle.log_mel(clips[i]))
+
+
+# --------------------------------------------------------- fp32 tower stages
+
+@pytest.fixture(scope="module")
+def model1_f32():
+    return ae.Model(weights(1), dtype="f32")
+
+
+def test_subsample_tone_fp32(model1_f32):
+    say("[gpu] subsample: 1 s tone, fp32")
+    x = synth.tone_clip(0)
+    mel_o = oracle.log_mel(x)
+    mel = cuda(mel_o)
+    g = ae.subsample(model1_f32, mel, np.array([0, 99])).cpu().numpy()
+    want = oracle.subsample(mel_o.astype(np.float32), weights(1))
+    assert g.shape == (25, 1024)
+    assert rel_l2(g, want) <= FP32_TOL, rel_l2(g, want)
+
+
+def test_subsample_ragged_fp32(model1_f32):
+    say("[gpu] subsample: ragged frame counts (1, 2, 3, 5, 99, 2999), fp32")
+    rng = np.random.default_rng(11)
+    Fs = [1, 2, 3, 5, 99, 2999, 0, 4]
+    mels = [rng.standard_normal((f, 128)).astype(np.float32) for f in Fs]
+    fo = np.concatenate([[0], np.cumsum(Fs)])
+    g = ae.subsample(model1_f32, cuda(np.concatenate(mels)), fo).cpu().numpy()
+    off = 0
+    for m, f in zip(mels, Fs):
+        t = -(-(-(-f // 2)) // 2)
+        if t:
+            want = oracle.subsample(m, weights(1))
+            assert rel_l2(g[off:off + t], want) <= FP32_TOL, (f, rel_l2(g[off:off + t], want))
+        off += t
+    assert off == g.shape[0]
+
+
+def test_layer_tone_fp32(model1_f32):
+    say("[gpu] conformer_layer: 1 layer on the tone clip's tokens, fp32")
+    W = weights(1)
+    x = synth.tone_clip(0)
+    h0 = oracle.subsample(oracle.log_mel(x), W).astype(np.float32)
+    pos = np.arange(25, dtype=np.int32)
+    h = cuda(h0)
+    ae.conformer_layer(model1_f32, 0, h, cuda(pos, torch.int32))
+    want = oracle.conformer_layer(h0, W["layers"][0], pos)
+    assert rel_l2(h.cpu().numpy(), want) <= FP32_TOL, rel_l2(h.cpu().numpy(), want)
+
+
+def test_layer_packed_positions_fp32(model1_f32):
+    """Two clips packed: masks must not cross the boundary."""
+    say("[gpu] conformer_layer: packed clips of 7 and 30 tokens, fp32")
+    W = weights(1)
+    rng = np.random.default_rng(12)
+    h0 = rng.standard_normal((37, 1024)).astype(np.float32)
+    pos = np.concatenate([np.arange(7), np.arange(30)]).astype(np.int32)
+    h = cuda(h0)
+    ae.conformer_layer(model1_f32, 0, h, cuda(pos, torch.int32))
+    want = oracle.conformer_layer(h0, W["layers"][0], pos)
+    g = h.cpu().numpy()
+    assert rel_l2(g[:7], want[:7]) <= FP32_TOL and rel_l2(g[7:], want[7:]) <= FP32_TOL
+
+
+def test_layer_clamps_and_softcap_bind_fp32():
+    """Bounds of +-0.5 make every clamp bind; large q weights and
+    per_dim_scale above 20 (softplus pass-through) push logits past the
+    cap; q, k, v get different input bounds."""
+    say("[gpu] conformer_layer: clamps +-0.5, softcap binding, distinct q/k/v input clamps")
+    W = synth.make_weights(layers=1, clip=(-0.5, 0.5, -0.5, 0.5))
+    L = W["layers"][0]
+    L["q"] = (L["q"] * 40).astype(np.float32)
+    L["q_clip"] = (-3.0, 3.0, -math.inf, math.inf)
+    L["k_clip"] = (-2.0, 2.0, -math.inf, math.inf)
+    L["v_clip"] = (-1.0, 1.0, -0.25, 0.25)
+    pds = L["per_dim_scale"].copy()
+    pds[::2] = 21.0 + np.arange(64) * 0.1
+    L["per_dim_scale"] = pds
+    m = ae.Model(W, dtype="f32")
+    rng = np.random.default_rng(13)
+    h0 = rng.standard_normal((40, 1024)).astype(np.float32)
+    pos = np.arange(40, dtype=np.int32)
+    h = cuda(h0)
+    ae.conformer_layer(m, 0, h, cuda(pos, torch.int32))
+    want = oracle.conformer_layer(h0, L, pos)
+    assert rel_l2(h.cpu().numpy(), want) <= FP32_TOL, rel_l2(h.cpu().numpy(), want)
+
+
+# ----------------------------------------------------------- whole encoder
+
+def test_encode_tone_one_layer_fp32():
+    say("[gpu] encode: 1 s tone, 1 layer + head, fp32, per-stage trace")
+    W = weights(1)
+    m = ae.Model(W, dtype="f32")
+    x = synth.tone_clip(0)
+    wave, so = synth.pack([x])
+    out, tr = ae.encode(m, cuda(wave), so, trace=True)
+    otr = []
+    want = oracle.encode_clips([x], W, trace=otr)[0]
+    assert rel_l2(tr[0].cpu().numpy(), otr[0]) <= FP32_TOL
+    assert rel_l2(tr[1].cpu().numpy(), otr[1]) <= FP32_TOL
+    assert rel_l2(out.cpu().numpy(), want) <= FP32_TOL, rel_l2(out.cpu().numpy(), want)
+
+
+def test_encode_30s_twelve_layers_fp32():
+    say("[gpu] encode: one 30 s multisine clip, 12 layers + head, fp32")
+    W = weights(12)
+    m = ae.Model(W, dtype="f32")
+    x = synth.multisine_clip(0)
+    wave, so = synth.pack([x])
+    out, tr = ae.encode(m, cuda(wave), so, trace=True)
+    otr = []
+    want = oracle.encode_clips([x], W, trace=otr)[0]
+    assert out.shape == (750, 512)
+    for i in range(13):
+        r = rel_l2(tr[i].cpu().numpy(), otr[i])
+        say(f"    stage {i}: rel {r:.3e}")
+        assert r <= FP32_TOL, (i, r)
+    r = rel_l2(out.cpu().numpy(), want)
+    say(f"    output: rel {r:.3e}")
+    assert r <= FP32_TOL
+
+
+def test_encode_batch32_bf16_sampled():
+    """The benchmark workload: 32 x 30 s, bf16 weights and operands."""
+    say("[gpu] encode: 32 x 30 s multisine, bf16, clips 0 and 31 vs oracle")
+    W = weights(12, bf16=True)
+    m = ae.Model(W, dtype="bf16")
+    clips = synth.multisine_batch(32)
+    wave, so = synth.pack(clips)
+    out = ae.encode(m, cuda(wave), so).cpu().numpy()
+    assert out.shape == (24000, 512)
+    for i in (0, 31):
+        want = oracle.encode_clips([clips[i]], W)[0]
+        r = rel_l2(out[i * 750:(i + 1) * 750], want)
+        say(f"    clip {i}: rel {r:.3e}, max-rel {rel_max(out[i * 750:(i + 1) * 750], want):.3e}")
+        assert r <= BF16_TOL
+
+
+def test_encode_ragged64_bf16_sampled():
+    say("[gpu] encode: 64 ragged pink-noise clips, bf16, shortest/longest/middle vs oracle")
+    W = weights(12, bf16=True)
+    m = ae.Model(W, dtype="bf16")
+    clips = synth.ragged_batch(64)
+    wave, so = synth.pack(clips)
+    out = ae.encode(m, cuda(wave), so).cpu().numpy()
+    T = [oracle.num_tokens(len(c)) for c in clips]
+    toff = np.concatenate([[0], np.cumsum(T)])
+    assert out.shape[0] == toff[-1]
+    lens = [len(c) for c in clips]
+    for i in sorted({int(np.argmin(lens)), int(np.argmax(lens)), 32}):
+        want = oracle.encode_clips([clips[i]], W)[0]
+        r = rel_l2(out[toff[i]:toff[i + 1]], want)
+        say(f"    clip {i} ({lens[i]} samples): rel {r:.3e}")
+        assert r <= BF16_TOL
+
+
+# -------------------------------------------------------------- invariants
+
+def test_causality_bf16():
+    """Token j reads samples <= 640 j + 639: perturbing later samples
+    leaves tokens 0..j bit-identical on the GPU."""
+    say("[gpu] invariant: causality, bf16")
+    W = weights(12, bf16=True)
+    m = ae.Model(W, dtype="bf16")
+    x = synth.multisine_clip(3, 64000)
+    j = 40
+    y = x.copy()
+    y[640 * j + 640:] += np.float32(0.25)
+    a = ae.encode(m, cuda(x), np.array([0, len(x)])).cpu().numpy()
+    b = ae.encode(m, cuda(y), np.array([0, len(y)])).cpu().numpy()
+    assert np.array_equal(a[:j + 1], b[:j + 1])
+    assert not np.array_equal(a[j + 1], b[j + 1])
+
+
+def test_clip_isolation_and_determinism_bf16():
+    say("[gpu] invariant: clip isolation in a pack, determinism, bf16")
+    W = weights(12, bf16=True)
+    m = ae.Model(W, dtype="bf16")
+    clips = [synth.pink_clip(1, 30000), synth.tone_clip(2, 150), synth.multisine_clip(4, 50000)]
+    wave, so = synth.pack(clips)
+    packed = ae.encode(m, cuda(wave), so).cpu().numpy()
+    again = ae.encode(m, cuda(wave), so).cpu().numpy()
+    assert np.array_equal(packed, again)
+    T = [ae.num_tokens(len(c)) for c in clips]
+    assert T[1] == 0
+    off = 0
+    for c, t in zip(clips, T):
+        alone = ae.encode(m, cuda(c), np.array([0, len(c)])).cpu().numpy() if t else np.zeros((0, 512))
+        assert np.array_equal(alone, packed[off:off + t])
+        off += t
+
+
+def test_empty_batches():
+    say("[gpu] edge: empty batch, clips without tokens")
+    W = weights(1)
+    m = ae.Model(W, dtype="f32")
+    out = ae.encode(m, cuda(np.zeros(0, np.float32)), np.array([0]))
+    assert out.shape == (0, 512)
+    out = ae.encode(m, cuda(np.zeros(300, np.float32)), np.array([0, 100, 260, 300]))
+    assert out.shape == (0, 512)
+    x = synth.tone_clip(0, 161)
+    out = ae.encode(m, cuda(x), np.array([0, 161]))
+    want = oracle.encode_clips([x], W)[0]
+    assert out.shape == (1, 512) and rel_l2(out.cpu().numpy(), want) <= FP32_TOL

@@ -1,0 +1,109 @@
+"""CPU checks of the C-ABI library: it loads, exports every symbol
+include/ae.h declares, its host-only functions agree bit-exactly with the
+oracle's integer functions, and argument errors are reported before any
+device work (no call here touches a GPU)."""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+from log_mel_conformer_amd import ae
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "ae.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(ae_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = ae.lib()
+    names = _declared()
+    assert len(names) >= 15, names
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_counts_match_oracle():
+    for n in list(range(0, 3000)) + list(range(470000, 490000, 7)) + [10 ** 7, -5]:
+        assert ae.num_frames(n) == (oracle.num_frames(n) if n >= 0 else 0), n
+        assert ae.num_tokens(n) == (oracle.num_tokens(n) if n >= 0 else 0), n
+
+
+def test_plan_prefix_sums():
+    lens = [100, 161, 16000, 560000, 0, 72825]
+    p = ae.plan(lens)
+    F = [oracle.num_frames(n) for n in lens]
+    T = [oracle.num_tokens(n) for n in lens]
+    assert np.array_equal(p["frame_off"], np.concatenate([[0], np.cumsum(F)]))
+    assert np.array_equal(p["token_off"], np.concatenate([[0], np.cumsum(T)]))
+    assert np.array_equal(p["sample_off"], np.concatenate([[0], np.cumsum(np.minimum(lens, 480000))]))
+    assert np.array_equal(p["row_off"], np.concatenate([[0], np.cumsum([-(-f // 2) for f in F])]))
+    with pytest.raises(ae.AeError) as e:
+        ae.plan([5, -1])
+    assert e.value.status == ae.AE_ERR_INVALID
+
+
+def _fake_weights(cfg):
+    """A weight table whose pointers are never dereferenced (validation
+    fails before any device work)."""
+    layers = (ae.LayerWeights * cfg.layers)()
+    fake = C.c_void_p(0x10000)
+    for i in range(cfg.layers):
+        for name, typ in ae.LAYER_FIELDS:
+            if typ is ae.Clip:
+                setattr(layers[i], name, ae.Clip(-8, 8, -8, 8))
+            else:
+                setattr(layers[i], name, fake)
+    W = ae.Weights()
+    for f in ("conv0", "ln0", "conv1", "ln1", "in_proj", "out_proj", "out_bias", "embed"):
+        setattr(W, f, fake)
+    W.layers = layers
+    return W
+
+
+def _create(cfg, W):
+    h = C.c_void_p()
+    st = ae.lib().ae_model_create(C.byref(cfg), C.byref(W), ae.AE_BF16, None, C.byref(h))
+    return st, h
+
+
+def test_model_create_refuses_before_device_work():
+    cfg = ae.default_config(layers=1, ctx_right=1)
+    st, h = _create(cfg, _fake_weights(cfg))
+    assert st == ae.AE_ERR_UNSUPPORTED and h.value is None
+    assert b"context_right" in ae.lib().ae_last_error()
+    cfg = ae.default_config(layers=1, hidden=512)
+    assert _create(cfg, _fake_weights(cfg))[0] == ae.AE_ERR_UNSUPPORTED
+    cfg = ae.default_config(layers=1)
+    W = _fake_weights(cfg)
+    W.layers[0].v = None
+    st, _ = _create(cfg, W)
+    assert st == ae.AE_ERR_INVALID and b"layer 0: weight v" in ae.lib().ae_last_error()
+    W = _fake_weights(cfg)
+    W.layers[0].q_clip = ae.Clip(1.0, -1.0, -8, 8)
+    assert _create(cfg, W)[0] == ae.AE_ERR_INVALID
+
+
+def test_logmel_refuses_small_workspace_before_device_work():
+    so = np.array([0, 16000], np.int64)
+    fake = C.c_void_p(0x10000)
+    st = ae.lib().ae_logmel(fake, so.ctypes.data_as(C.POINTER(C.c_int64)), 1, fake, fake, 8, None)
+    assert st == ae.AE_ERR_CAPACITY
+    bad = np.array([0, 100, 50], np.int64)
+    st = ae.lib().ae_logmel(fake, bad.ctypes.data_as(C.POINTER(C.c_int64)), 2, fake, fake, 1 << 20, None)
+    assert st == ae.AE_ERR_INVALID
+    # clips of <= 160 samples have no frames: nothing to do, not an error
+    tiny = np.array([0, 160, 200], np.int64)
+    st = ae.lib().ae_logmel(None, tiny.ctypes.data_as(C.POINTER(C.c_int64)), 2, None, None, 0, None)
+    assert st == ae.AE_OK
+
+
+def test_timing_class_validation():
+    assert ae.lib().ae_timing_enable(99) == ae.AE_ERR_INVALID
+    assert ae.lib().ae_timing_enable(-1) == ae.AE_OK
