@@ -396,7 +396,8 @@ ae_status subsample_impl(const ae_model* m, const float* mel, const Plan& pl, co
 // clamp(rms(h) * ff1_pre); if `next` is given, the layer's last row kernel
 // also writes the next layer's first input that way.
 ae_status layer_impl(const ae_model* m, int l, float* h, const int32_t* pos, int64_t n,
-                     const Ws& w, hipStream_t s, bool pre_done, const ae_layer_weights* next) {
+                     const Ws& w, hipStream_t s, bool pre_done, const ae_layer_weights* next,
+                     void* h_copy) {
   const ae_layer_weights& L = m->layers[l];
   const int d = m->cfg.hidden, ff = m->cfg.ff;
   const int M = (int)n;
@@ -491,6 +492,7 @@ ae_status layer_impl(const ae_model* m, int l, float* h, const int32_t* pos, int
     RowNormParams r = rn_params(n, d, h);
     r.y = w.y; r.scale = m->cfg.residual_weight; r.w_post = L.ff2_post;
     r.w_out = L.norm_out;
+    r.h_copy = h_copy;
     if (next) {
       r.w_next = next->ff1_pre; r.n_out = 1; r.a[0] = w.a[0];
       r.lo[0] = next->ff1_w1_clip.in_lo; r.hi[0] = next->ff1_w1_clip.in_hi;
@@ -773,7 +775,7 @@ ae_status ae_conformer_layer(const ae_model* m, int32_t layer, float* h, const i
   if ((st = check_sizes(m, n, 0)) != AE_OK) return st;
   Ws w = ws_layout(m, 1, 0, n, (char*)ws);
   if ((st = check_ws(ws, ws_bytes, w.total)) != AE_OK) return st;
-  return layer_impl(m, layer, h, pos, n, w, (hipStream_t)stream, false, nullptr);
+  return layer_impl(m, layer, h, pos, n, w, (hipStream_t)stream, false, nullptr, nullptr);
 }
 
 ae_status ae_encode(const ae_model* m, const float* wave, const int64_t* sample_off, int32_t B,
@@ -799,14 +801,17 @@ ae_status ae_encode(const ae_model* m, const float* wave, const int64_t* sample_
   const int L = m->cfg.layers;
   for (int l = 0; l < L; ++l) {
     const ae_layer_weights* next = (l + 1 < L) ? &m->layers[l + 1] : nullptr;
-    if ((st = layer_impl(m, l, w.h, w.tok_pos, T, w, s, l > 0, next)) != AE_OK) return st;
+    // in bf16 the head's GEMM reads a bf16 copy of the final residual stream
+    void* hc = (l + 1 == L && m->dt == AE_BF16) ? w.a[0] : nullptr;
+    if ((st = layer_impl(m, l, w.h, w.tok_pos, T, w, s, l > 0, next, hc)) != AE_OK) return st;
     if (trace && trace[1 + l])
       AE_HIP_TRY(hipMemcpyAsync(trace[1 + l], w.h, hbytes, hipMemcpyDeviceToDevice, s));
   }
   // head: output_proj + bias, weightless RMS norm, embed_audio
   const int oh = m->cfg.out_hidden, od = m->cfg.out_dim;
   {
-    GemmParams p = gemm_params((int)T, oh, d, w.h, d, m->w.out_proj, d, w.o1, oh);
+    const void* hin = m->dt == AE_BF16 ? w.a[0] : (const void*)w.h;
+    GemmParams p = gemm_params((int)T, oh, d, hin, d, m->w.out_proj, d, w.o1, oh);
     p.bias = m->w.out_bias;
     AE_LAUNCH(AE_K_GEMM_HEAD, s, launch_gemm(m->dt, EPI_BIAS, A_PLAIN, false, p, s));
   }

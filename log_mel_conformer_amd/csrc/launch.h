@@ -61,7 +61,7 @@ hipError_t launch_conv0(ae_dtype dt, const float* mel, const int64_t* frame_off,
 // For each row of h [n][d]:
 //   if y:     h += scale * rms(y) * w_post
 //   if w_out: h  = rms(h) * w_out
-//   store h (when y or w_out was applied)
+//   store h (when y or w_out was applied); if h_copy: also h as dtype dt
 //   if w_next: a_i = clamp(rms(h) * w_next, lo_i, hi_i) for i < n_out (dtype dt)
 // With w_next = nullptr and h_in_place false, nothing but the a_i are written.
 struct RowNormParams {
@@ -77,6 +77,7 @@ struct RowNormParams {
   void* a[3];
   float lo[3], hi[3];
   int n_out;
+  void* h_copy;          // if set: the final h also stored here in dtype dt
 };
 hipError_t launch_rownorm(ae_dtype dt, const RowNormParams& p, hipStream_t s);
 

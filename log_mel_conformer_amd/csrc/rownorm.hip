@@ -68,6 +68,11 @@ __global__ void __launch_bounds__(256) k_rownorm(RowNormParams p) {
       *(float4*)(hrow + q * 256 + lane * 4) =
           make_float4(x[4 * q], x[4 * q + 1], x[4 * q + 2], x[4 * q + 3]);
   }
+  if (p.h_copy) {
+    T* crow = (T*)p.h_copy + row * d;
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) crow[(i >> 2) * 256 + lane * 4 + (i & 3)] = from_f32<T>(x[i]);
+  }
   if (p.w_next || p.plain_next) {
     float ss = 0.f;
 #pragma unroll

@@ -217,8 +217,13 @@ def test_encode_batch32_bf16_sampled():
     m = ae.Model(W, dtype="bf16")
     clips = synth.multisine_batch(32)
     wave, so = synth.pack(clips)
-    out = ae.encode(m, cuda(wave), so).cpu().numpy()
+    out, tr = ae.encode(m, cuda(wave), so, trace=True)
+    out = out.cpu().numpy()
     assert out.shape == (24000, 512)
+    otr = []
+    oracle.encode_clips([clips[0]], W, trace=otr)
+    for k in range(13):
+        say(f"    clip 0 stage {k}: rel {rel_l2(tr[k][:750].cpu().numpy(), otr[k]):.3e}")
     for i in (0, 31):
         want = oracle.encode_clips([clips[i]], W)[0]
         r = rel_l2(out[i * 750:(i + 1) * 750], want)
