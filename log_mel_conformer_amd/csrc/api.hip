@@ -24,6 +24,7 @@ struct ae_model {
   float* R = nullptr;         // [layers][n_dist][hidden]
   float* colscale = nullptr;  // [layers][3 hidden]
   void* conv1r = nullptr;     // [32][9 * 128], model dtype
+  float* dwt = nullptr;       // [layers][conv_kernel][hidden]: light-conv taps transposed
   std::vector<int> attn_nout;  // distinct input clamps among q, k, v (1..3)
 };
 
@@ -144,7 +145,19 @@ __global__ void k_conv1_reorder(const T* __restrict__ w, T* __restrict__ wr) {
   wr[co * kC0 * 9 + tap * kC0 + ci] = w[i];
 }
 
+__global__ void k_transpose_taps(const float* w, int d, int K, float* wt) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= d * K) return;
+  const int c = i / K, k = i - c * K;
+  wt[k * d + c] = w[i];
+}
+
 }  // namespace
+
+hipError_t launch_transpose_taps(const float* w, int d, int K, float* wt, hipStream_t s) {
+  hipLaunchKernelGGL(k_transpose_taps, dim3((d * K + 255) / 256), dim3(256), 0, s, w, d, K, wt);
+  return hipGetLastError();
+}
 
 hipError_t launch_write_i64(int64_t* dst, const int64_t* vals, int count, hipStream_t s) {
   for (int off = 0; off < count; off += 64) {
@@ -271,7 +284,7 @@ struct Ws {
   float* h = nullptr;
   void* a[3] = {nullptr, nullptr, nullptr};
   void* u = nullptr;
-  float* y = nullptr;
+  void* y = nullptr;  // GEMM outputs feeding a post-norm, model dtype
   void* qkv = nullptr;
   void* o = nullptr;
   void* g = nullptr;
@@ -303,7 +316,7 @@ Ws ws_layout(const ae_model* m, int B, int64_t F, int64_t T, char* base) {
   w.h = (float*)take(sizeof(float) * (size_t)T * d);
   for (int i = 0; i < 3; ++i) w.a[i] = take(es * (size_t)T * d);
   w.u = take(es * (size_t)T * m->cfg.ff);
-  w.y = (float*)take(sizeof(float) * (size_t)T * d);
+  w.y = take(es * (size_t)T * d);
   w.qkv = take(es * (size_t)T * 3 * d);
   w.o = take(es * (size_t)T * d);
   w.g = take(es * (size_t)T * d);
@@ -418,7 +431,7 @@ ae_status layer_impl(const ae_model* m, int l, float* h, const int32_t* pos, int
     AE_LAUNCH(AE_K_GEMM_FFN1, s, launch_gemm(dt, EPI_SILU, A_PLAIN, lowp, p1, s));
     GemmParams p2 = gemm_params(M, d, ff, w.u, ff, w2, ff, w.y, d);
     set_out_clip(p2, c2);
-    AE_LAUNCH(AE_K_GEMM_FFN2, s, launch_gemm(dt, EPI_STORE, A_PLAIN, false, p2, s));
+    AE_LAUNCH(AE_K_GEMM_FFN2, s, launch_gemm(dt, EPI_STORE, A_PLAIN, lowp, p2, s));
     return AE_OK;
   };
 
@@ -461,7 +474,7 @@ ae_status layer_impl(const ae_model* m, int l, float* h, const int32_t* pos, int
   {
     GemmParams p = gemm_params(M, d, d, w.o, d, L.post, d, w.y, d);
     set_out_clip(p, L.post_clip);
-    AE_LAUNCH(AE_K_GEMM_POST, s, launch_gemm(dt, EPI_STORE, A_PLAIN, false, p, s));
+    AE_LAUNCH(AE_K_GEMM_POST, s, launch_gemm(dt, EPI_STORE, A_PLAIN, lowp, p, s));
   }
   {
     RowNormParams r = rn_params(n, d, h);
@@ -478,7 +491,8 @@ ae_status layer_impl(const ae_model* m, int l, float* h, const int32_t* pos, int
     AE_LAUNCH(AE_K_GEMM_LCSTART, s, launch_gemm(dt, EPI_GLU, A_PLAIN, lowp, p, s));
   }
   AE_LAUNCH(AE_K_LCONV, s,
-            launch_lconv(dt, w.g, L.lc_dw, m->cfg.conv_kernel, L.lc_norm, pos, n, d,
+            launch_lconv(dt, w.g, m->dwt + (size_t)l * m->cfg.conv_kernel * d, m->cfg.conv_kernel,
+                         L.lc_norm, pos, n, d,
                          L.lc_end_clip.in_lo, L.lc_end_clip.in_hi, w.c, s));
   {
     GemmParams p = gemm_params(M, d, d, w.c, d, L.lc_end, d, h, d);
@@ -693,11 +707,17 @@ ae_status ae_model_create(const ae_config* cfg, const ae_weights* w, ae_dtype dt
   if ((e = hipMalloc((void**)&m->colscale, sizeof(float) * (size_t)c.layers * 3 * c.hidden)) != hipSuccess)
     return fail(e, "hipMalloc(colscale)");
   if ((e = hipMalloc(&m->conv1r, es * kC1 * kC0 * 9)) != hipSuccess) return fail(e, "hipMalloc(conv1)");
+  if ((e = hipMalloc((void**)&m->dwt, sizeof(float) * (size_t)c.layers * c.conv_kernel * c.hidden)) !=
+      hipSuccess)
+    return fail(e, "hipMalloc(taps)");
   for (int l = 0; l < c.layers; ++l) {
     const ae_layer_weights& L = m->layers[l];
     if ((e = launch_relative_keys(dt, L.rel_k, c.hidden, n_dist,
                                   m->R + (size_t)l * n_dist * c.hidden, s)) != hipSuccess)
       return fail(e, "relative keys");
+    if ((e = launch_transpose_taps(L.lc_dw, c.hidden, c.conv_kernel,
+                                   m->dwt + (size_t)l * c.conv_kernel * c.hidden, s)) != hipSuccess)
+      return fail(e, "light-conv taps");
     if ((e = launch_qkv_scale(L.per_dim_scale, c.hidden, m->head_dim, m->q_scale, m->k_scale,
                               m->colscale + (size_t)l * 3 * c.hidden, s)) != hipSuccess)
       return fail(e, "qkv scale");
@@ -713,6 +733,7 @@ void ae_model_destroy(ae_model* m) {
   if (m->R) hipFree(m->R);
   if (m->colscale) hipFree(m->colscale);
   if (m->conv1r) hipFree(m->conv1r);
+  if (m->dwt) hipFree(m->dwt);
   delete m;
 }
 

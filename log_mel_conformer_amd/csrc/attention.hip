@@ -5,86 +5,144 @@
 // softcap * tanh(logit / softcap), and the output is the softmax-weighted
 // sum of v_{t-d}. q and k arrive already scaled by the projection epilogue.
 //
-// One block per (32 consecutive tokens, head): the K and V rows those
-// tokens can reach (32 + left - 1) and R[0..left) of the head are staged
-// in LDS as float; 8 lanes serve one token, 16 of the 128 dimensions each,
-// and the per-distance dot products reduce over those 8 lanes. Rows before
-// the packed buffer or past its end are staged as zeros and masked out, so
-// no uninitialised value can reach the weighted sum.
+// One block per (64 consecutive tokens, head). The K and V rows those
+// tokens can reach (64 + left - 1 of them) are staged in LDS in the storage
+// type (16-byte loads, rows padded to spread banks), R[0..left) of the head
+// as float. Four lanes serve one token, 32 of the 128 dimensions each: a
+// lane forms its partial logits for every distance, two cross-lane steps
+// give all four lanes the full logits, each lane runs the (identical)
+// softmax, then accumulates its 32 output dimensions. Rows before the
+// packed buffer or past its end are staged as zeros and masked out, so no
+// uninitialised value can reach the weighted sum.
 #include "launch.h"
 
 namespace ae {
 namespace {
 
-constexpr int QB = 32;          // tokens per block
+constexpr int QB = 64;          // tokens per block
 constexpr int HD = 128;         // head dim
 constexpr int MAXL = 12;        // largest window this kernel serves
 constexpr int HALO = MAXL - 1;
-constexpr int LDR = HD + 4;     // padded LDS row (floats)
+constexpr int ROWS = QB + HALO;
+constexpr int DPL = 32;         // dimensions per lane
+
+template <typename T> struct Stage;
+template <> struct Stage<bf16> {
+  static constexpr int LD = HD + 8;  // elements per LDS row (pad 16 bytes)
+};
+template <> struct Stage<float> {
+  static constexpr int LD = HD + 4;
+};
+
+__device__ __forceinline__ void load8(const bf16* p, float* v) {
+  const bf16x8 a = *(const bf16x8*)p;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = (float)a[i];
+}
+__device__ __forceinline__ void load8(const float* p, float* v) {
+  const float4 a = *(const float4*)p, b = *(const float4*)(p + 4);
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+  v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+__device__ __forceinline__ void store8(bf16* p, const float* v) {
+  bf16x8 a;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) a[i] = (bf16)v[i];
+  *(bf16x8*)p = a;
+}
+__device__ __forceinline__ void store8(float* p, const float* v) {
+  *(float4*)p = make_float4(v[0], v[1], v[2], v[3]);
+  *(float4*)(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
+}
+// copy 8 elements of storage type (16 or 32 bytes)
+__device__ __forceinline__ void copy8(bf16* d, const bf16* s) { *(bf16x8*)d = *(const bf16x8*)s; }
+__device__ __forceinline__ void copy8(float* d, const float* s) {
+  *(float4*)d = *(const float4*)s;
+  *(float4*)(d + 4) = *(const float4*)(s + 4);
+}
+__device__ __forceinline__ void zero8(bf16* d) {
+  bf16x8 z;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) z[i] = (bf16)0.f;
+  *(bf16x8*)d = z;
+}
+__device__ __forceinline__ void zero8(float* d) {
+  *(float4*)d = make_float4(0.f, 0.f, 0.f, 0.f);
+  *(float4*)(d + 4) = make_float4(0.f, 0.f, 0.f, 0.f);
+}
 
 template <typename T>
 __global__ void __launch_bounds__(256) k_attn(const T* __restrict__ qkv, const float* __restrict__ R,
                                               const int32_t* __restrict__ pos, int64_t n, int d,
                                               int left, float cap, float lo, float hi,
                                               T* __restrict__ o) {
-  __shared__ float Ks[QB + HALO][LDR];
-  __shared__ float Vs[QB + HALO][LDR];
-  __shared__ float Rs[MAXL][LDR];
+  constexpr int LD = Stage<T>::LD;
+  __shared__ __attribute__((aligned(16))) T Ks[ROWS * LD];
+  __shared__ __attribute__((aligned(16))) T Vs[ROWS * LD];
+  __shared__ __attribute__((aligned(16))) float Rs[MAXL * HD];
   const int h = blockIdx.y;
   const int64_t t0 = (int64_t)blockIdx.x * QB;
   const int tid = threadIdx.x;
   const int64_t ld = 3 * (int64_t)d;
-  for (int idx = tid; idx < (QB + HALO) * (HD / 4); idx += 256) {
-    const int rr = idx / (HD / 4), c4 = (idx - rr * (HD / 4)) * 4;
+  // stage K and V: rows t0 - HALO .. t0 + QB - 1, 8 elements per thread-step
+  for (int idx = tid; idx < ROWS * (HD / 8); idx += 256) {
+    const int rr = idx / (HD / 8), c = (idx - rr * (HD / 8)) * 8;
     const int64_t t = t0 - HALO + rr;
-    float kv[4] = {0.f, 0.f, 0.f, 0.f}, vv[4] = {0.f, 0.f, 0.f, 0.f};
     if (t >= 0 && t < n) {
-      const T* kp = qkv + t * ld + d + h * HD + c4;
-      const T* vp = qkv + t * ld + 2 * d + h * HD + c4;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        kv[e] = to_f32(kp[e]);
-        vv[e] = to_f32(vp[e]);
-      }
-    }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      Ks[rr][c4 + e] = kv[e];
-      Vs[rr][c4 + e] = vv[e];
+      copy8(&Ks[rr * LD + c], qkv + t * ld + d + h * HD + c);
+      copy8(&Vs[rr * LD + c], qkv + t * ld + 2 * d + h * HD + c);
+    } else {
+      zero8(&Ks[rr * LD + c]);
+      zero8(&Vs[rr * LD + c]);
     }
   }
-  for (int idx = tid; idx < MAXL * HD; idx += 256) {
-    const int dist = idx / HD, c = idx - dist * HD;
-    Rs[dist][c] = dist < left ? R[(int64_t)dist * d + h * HD + c] : 0.f;
+  for (int idx = tid; idx < MAXL * HD / 4; idx += 256) {
+    const int dist = idx / (HD / 4), c = (idx - dist * (HD / 4)) * 4;
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (dist < left) v = *(const float4*)(R + (int64_t)dist * d + h * HD + c);
+    *(float4*)&Rs[dist * HD + c] = v;
   }
   __syncthreads();
 
-  const int qi = tid >> 3, part = tid & 7;
+  const int qi = tid >> 2, part = tid & 3;
   const int64_t t = t0 + qi;
   const bool valid = t < n;
-  float q[16];
-  const T* qp = qkv + (valid ? t : 0) * ld + h * HD + part * 16;
+  const int c0 = part * DPL;
+  float q[DPL];
+  {
+    const T* qp = qkv + (valid ? t : 0) * ld + h * HD + c0;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) q[i] = valid ? to_f32(qp[i]) : 0.f;
+    for (int i = 0; i < DPL; i += 8) load8(qp + i, q + i);
+  }
   const int span = valid ? min(pos[t] + 1, left) : 1;
 
   float s[MAXL];
+#pragma unroll
+  for (int dist = 0; dist < MAXL; ++dist) {
+    const T* kr = &Ks[(qi + HALO - dist) * LD + c0];
+    const float* rr = &Rs[dist * HD + c0];
+    float acc = 0.f;
+#pragma unroll
+    for (int i = 0; i < DPL; i += 8) {
+      float kv[8];
+      load8(kr + i, kv);
+      const float4 r0 = *(const float4*)(rr + i), r1 = *(const float4*)(rr + i + 4);
+      acc += q[i] * (kv[0] + r0.x) + q[i + 1] * (kv[1] + r0.y) + q[i + 2] * (kv[2] + r0.z) +
+             q[i + 3] * (kv[3] + r0.w) + q[i + 4] * (kv[4] + r1.x) + q[i + 5] * (kv[5] + r1.y) +
+             q[i + 6] * (kv[6] + r1.z) + q[i + 7] * (kv[7] + r1.w);
+    }
+    s[dist] = acc;
+  }
+  // full logits in all four lanes of the token
+#pragma unroll
+  for (int dist = 0; dist < MAXL; ++dist) {
+    s[dist] += __shfl_xor(s[dist], 1, 64);
+    s[dist] += __shfl_xor(s[dist], 2, 64);
+  }
   float mx = -INFINITY;
 #pragma unroll
   for (int dist = 0; dist < MAXL; ++dist) {
-    const float* kr = &Ks[qi + HALO - dist][part * 16];
-    const float* rr = &Rs[dist][part * 16];
-    float ac = 0.f, bd = 0.f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      ac += q[i] * kr[i];
-      bd += q[i] * rr[i];
-    }
-    float logit = ac + bd;
-    logit += __shfl_xor(logit, 4, 64);
-    logit += __shfl_xor(logit, 2, 64);
-    logit += __shfl_xor(logit, 1, 64);
-    const float z = cap * tanhf(logit / cap);
+    const float z = cap * tanhf(s[dist] / cap);
     s[dist] = dist < span ? z : -INFINITY;
     mx = fmaxf(mx, s[dist]);
   }
@@ -95,20 +153,30 @@ __global__ void __launch_bounds__(256) k_attn(const T* __restrict__ qkv, const f
     den += s[dist];
   }
   const float rden = 1.0f / den;
-  float acc[16];
+  float acc[DPL];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+  for (int i = 0; i < DPL; ++i) acc[i] = 0.f;
 #pragma unroll
   for (int dist = 0; dist < MAXL; ++dist) {
     const float pd = s[dist] * rden;
-    const float* vr = &Vs[qi + HALO - dist][part * 16];
+    const T* vr = &Vs[(qi + HALO - dist) * LD + c0];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) acc[i] += pd * vr[i];
+    for (int i = 0; i < DPL; i += 8) {
+      float vv[8];
+      load8(vr + i, vv);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[i + e] += pd * vv[e];
+    }
   }
   if (valid) {
-    T* op = o + t * d + h * HD + part * 16;
+    T* op = o + t * d + h * HD + c0;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) op[i] = from_f32<T>(clampf(acc[i], lo, hi));
+    for (int i = 0; i < DPL; i += 8) {
+      float ov[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ov[e] = clampf(acc[i + e], lo, hi);
+      store8(op + i, ov);
+    }
   }
 }
 

@@ -6,15 +6,28 @@
 // computed, and the padding treats them as absent.
 //
 // One block per output row t1 (a pair of frames): the three mel rows it
-// reads (2 t1 - 1 .. 2 t1 + 1) are staged in LDS with a zero border; each
-// wavefront owns 16 of the 64 output frequencies and each lane two of the
-// 128 channels, so the channel statistics are wavefront reductions. The
-// output is channels-last [row][f][c], which is what conv1's implicit GEMM
-// gathers 16-byte chunks from.
+// reads (2 t1 - 1 .. 2 t1 + 1) are staged in LDS with a zero border. A lane
+// owns 8 consecutive channels of one output frequency; 16 lanes cover the
+// 128 channels of a frequency, so the channel statistics are 16-lane
+// reductions and each lane writes its 8 outputs as one vector. A wavefront
+// does 4 frequencies per pass, 16 per block row. The output is
+// channels-last [row][f][c], which is what conv1's implicit GEMM gathers
+// 16-byte chunks from.
 #include "launch.h"
 
 namespace ae {
 namespace {
+
+__device__ __forceinline__ void store8(float* p, const float* v) {
+  *(float4*)p = make_float4(v[0], v[1], v[2], v[3]);
+  *(float4*)(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
+}
+__device__ __forceinline__ void store8(bf16* p, const float* v) {
+  bf16x8 a;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) a[i] = (bf16)v[i];
+  *(bf16x8*)p = a;
+}
 
 template <typename T>
 __global__ void __launch_bounds__(256) k_conv0(const float* __restrict__ mel,
@@ -37,30 +50,48 @@ __global__ void __launch_bounds__(256) k_conv0(const float* __restrict__ mel,
   }
   __syncthreads();
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  float wa[9], wb[9];
+  const int fsub = lane >> 4, c0 = (lane & 15) * 8;
+  float wk[8][9], g[8];
 #pragma unroll
-  for (int k = 0; k < 9; ++k) {
-    wa[k] = w0[lane * 9 + k];
-    wb[k] = w0[(lane + 64) * 9 + k];
+  for (int c = 0; c < 8; ++c) {
+#pragma unroll
+    for (int k = 0; k < 9; ++k) wk[c][k] = w0[(c0 + c) * 9 + k];
+    g[c] = g0[c0 + c];
   }
-  const float ga = g0[lane], gb = g0[lane + 64];
-  for (int f = w * 16; f < w * 16 + 16; ++f) {
-    float a = 0.f, b = 0.f;
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int f = w * 16 + it * 4 + fsub;
+    float x[9];
 #pragma unroll
     for (int dt = 0; dt < 3; ++dt)
 #pragma unroll
-      for (int df = 0; df < 3; ++df) {
-        const float x = m[dt][2 * f + df];  // column 2f + df - 1, shifted by the border
-        a += wa[dt * 3 + df] * x;
-        b += wb[dt * 3 + df] * x;
-      }
-    const float mean = wave_sum(a + b) * (1.0f / kC0);
-    const float da = a - mean, db = b - mean;
-    const float var = wave_sum(da * da + db * db) * (1.0f / kC0);
-    const float inv = rsqrtf(var + kEps);
-    T* out = y0 + ((size_t)r * kF1 + f) * kC0;
-    out[lane] = from_f32<T>(fmaxf(da * inv * ga, 0.f));
-    out[lane + 64] = from_f32<T>(fmaxf(db * inv * gb, 0.f));
+      for (int df = 0; df < 3; ++df) x[dt * 3 + df] = m[dt][2 * f + df];  // column 2f+df-1, shifted
+    float a[8];
+    float sum = 0.f;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      float acc = 0.f;
+#pragma unroll
+      for (int k = 0; k < 9; ++k) acc += wk[c][k] * x[k];
+      a[c] = acc;
+      sum += acc;
+    }
+#pragma unroll
+    for (int o = 8; o > 0; o >>= 1) sum += __shfl_xor(sum, o, 64);
+    const float mean = sum * (1.0f / kC0);
+    float q = 0.f;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      a[c] -= mean;
+      q += a[c] * a[c];
+    }
+#pragma unroll
+    for (int o = 8; o > 0; o >>= 1) q += __shfl_xor(q, o, 64);
+    const float inv = rsqrtf(q * (1.0f / kC0) + kEps);
+    float o8[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) o8[c] = fmaxf(a[c] * inv * g[c], 0.f);
+    store8(y0 + ((size_t)r * kF1 + f) * kC0 + c0, o8);
   }
 }
 

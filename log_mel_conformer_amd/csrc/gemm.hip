@@ -42,10 +42,123 @@ template <> struct Mma<float> {
   }
 };
 
-__device__ __forceinline__ int swz(int row, int c) { return row * ROWB + ((c ^ (row & 7)) << 4); }
+// LDS image of a tile row: chunk c of row r sits at chunk c ^ ((r >> 1) & 7).
+// The LDS has 64 four-byte banks (256 bytes), i.e. two 128-byte rows; a
+// 16-byte fragment read serves 16 lanes (16 consecutive rows, one chunk
+// index) per pass, and this XOR gives those 16 rows 16 distinct 16-byte
+// bank groups.
+__device__ __forceinline__ int swz(int row, int c) {
+  return row * ROWB + ((c ^ ((row >> 1) & 7)) << 4);
+}
 
 template <typename TO> __device__ __forceinline__ void store_out(TO* C, size_t idx, float v) {
   C[idx] = from_f32<TO>(v);
+}
+
+// Four consecutive outputs of one row, as one 16-byte (float) or 8-byte
+// (bf16) store.
+__device__ __forceinline__ void store4(float* p, float a, float b, float c, float d) {
+  *(float4*)p = make_float4(a, b, c, d);
+}
+__device__ __forceinline__ void store4(bf16* p, float a, float b, float c, float d) {
+  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+  bf16x4 v = {(bf16)a, (bf16)b, (bf16)c, (bf16)d};
+  *(bf16x4*)p = v;
+}
+
+// Epilogue of a wavefront's tile at (row0, col0). The MFMAs take the B
+// fragment as their first operand, so each 32x32 accumulator holds the
+// transposed sub-tile: acc[i][j][v] is C at row row0 + 32 i + lane % 32 and
+// column col0 + 32 j + (v / 4) * 8 + (lane / 32) * 4 + v % 4. A lane thus
+// owns four runs of four consecutive columns of one row per sub-tile, which
+// it writes as vector stores.
+template <typename TO, int MT, int NTL, int EPI>
+__device__ __forceinline__ void epilogue(const GemmParams& p, f32x16 (&acc)[MT][NTL], int row0,
+                                         int col0, int seg, int lane) {
+  TO* C = (TO*)p.C;
+  const int r = lane & 31, h = lane >> 5;
+#pragma unroll
+  for (int i = 0; i < MT; ++i) {
+    const int row = row0 + i * 32 + r;
+    const bool ok = row < p.M;
+    TO* crow = C + (size_t)(ok ? row : 0) * p.ldc;
+    if (EPI == EPI_GLU) {
+      const float lo = p.olo[0], hi = p.ohi[0];
+#pragma unroll
+      for (int jp = 0; jp < NTL / 2; ++jp)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int col = col0 / 2 + jp * 32 + g * 8 + h * 4;
+          float o[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float a = clampf(acc[i][2 * jp][4 * g + e], lo, hi);
+            const float b = clampf(acc[i][2 * jp + 1][4 * g + e], lo, hi);
+            o[e] = a * sigmoidf_(b);
+          }
+          if (ok) store4(crow + col, o[0], o[1], o[2], o[3]);
+        }
+    } else if (EPI == EPI_LNRELU) {
+      // the row's 32 channels: 16 in this lane, 16 in lane ^ 32
+      float sum = 0.f;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) sum += acc[i][0][v];
+      sum += __shfl_xor(sum, 32, 64);
+      const float mean = sum * (1.0f / 32);
+      float q = 0.f;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const float dx = acc[i][0][v] - mean;
+        q += dx * dx;
+      }
+      q += __shfl_xor(q, 32, 64);
+      const float inv = rsqrtf(q * (1.0f / 32) + kEps);
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int col = g * 8 + h * 4;
+        float o[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          o[e] = fmaxf((acc[i][0][4 * g + e] - mean) * inv * p.gain[col + e], 0.0f);
+        if (ok) store4(crow + col, o[0], o[1], o[2], o[3]);
+      }
+    } else {
+      const float lo = p.olo[seg], hi = p.ohi[seg];
+#pragma unroll
+      for (int j = 0; j < NTL; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int col = col0 + j * 32 + g * 8 + h * 4;
+          float x[4] = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                        acc[i][j][4 * g + 3]};
+          if (EPI == EPI_STORE) {
+            float4 sc = make_float4(1.f, 1.f, 1.f, 1.f);
+            if (p.colscale) sc = *(const float4*)(p.colscale + col);
+            if (ok)
+              store4(crow + col, clampf(x[0], lo, hi) * sc.x, clampf(x[1], lo, hi) * sc.y,
+                     clampf(x[2], lo, hi) * sc.z, clampf(x[3], lo, hi) * sc.w);
+          } else if (EPI == EPI_SILU) {
+            float o[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float y = clampf(x[e], lo, hi);
+              o[e] = clampf(y * sigmoidf_(y), p.nlo, p.nhi);
+            }
+            if (ok) store4(crow + col, o[0], o[1], o[2], o[3]);
+          } else if (EPI == EPI_RESID) {
+            float* hp = (float*)crow + col;
+            if (ok) {
+              const float4 hv = *(const float4*)hp;
+              store4(hp, hv.x + clampf(x[0], lo, hi), hv.y + clampf(x[1], lo, hi),
+                     hv.z + clampf(x[2], lo, hi), hv.w + clampf(x[3], lo, hi));
+            }
+          } else if (EPI == EPI_BIAS) {
+            const float4 bv = *(const float4*)(p.bias + col);
+            if (ok) store4((float*)crow + col, x[0] + bv.x, x[1] + bv.y, x[2] + bv.z, x[3] + bv.w);
+          }
+        }
+    }
+  }
 }
 
 template <typename T, typename TO, int BM, int BN, int WM, int WN, int AL, int EPI>
@@ -186,80 +299,260 @@ __global__ void __launch_bounds__(WM * WN * 64) k_gemm(GemmParams p) {
 #pragma unroll
       for (int i = 0; i < MT; ++i)
 #pragma unroll
-        for (int j = 0; j < NTL; ++j) Mma<T>::run(acc[i][j], fa[i], fb[j]);
+        for (int j = 0; j < NTL; ++j) Mma<T>::run(acc[i][j], fb[j], fa[i]);
     }
     if (kt + 1 < nk) store_lds(cur ^ 1);
     __syncthreads();
   }
 
-  // ---- epilogue. acc[i][j][v] sits at row (v/4)*8 + (lane/32)*4 + v%4 and
-  // column lane%32 of the 32x32 sub-tile (i, j).
-  TO* C = (TO*)p.C;
-  const int rbase = m0 + wm * WTM + (lane >> 5) * 4;
-  const int cl = lane & 31;
-  if (EPI == EPI_GLU) {
-    const float lo = p.olo[0], hi = p.ohi[0];
+  epilogue<TO, MT, NTL, EPI>(p, acc, m0 + wm * WTM, n0 + wn * WTN, seg, lane);
+}
+
+// Map the hardware block index to a tile. The dispatcher deals blocks to
+// the 8 XCDs round-robin; the blocks of one XCD get one contiguous range of
+// tile numbers, and tile numbers walk column-major through bands of GM row
+// tiles, so the ~32 blocks an XCD runs at once cover a GM x (32/GM) window
+// whose A and B slices are shared through that XCD's L2.
+template <int GM>
+__device__ __forceinline__ void tile_of(int b, int nblk, int tiles_m, int tiles_n, int& tm,
+                                        int& tn) {
+  const int per = nblk >> 3, rem = nblk & 7;
+  const int xcd = b & 7, local = b >> 3;
+  const int t = xcd < rem ? xcd * (per + 1) + local : rem * (per + 1) + (xcd - rem) * per + local;
+  const int band = t / (GM * tiles_n);
+  const int m_lo = band * GM;
+  const int gm = min(GM, tiles_m - m_lo);
+  const int r = t - band * GM * tiles_n;
+  tn = r / gm;
+  tm = m_lo + (r - tn * gm);
+}
+
+// s_waitcnt vmcnt(N) with every other counter left alone (gfx9 encoding:
+// vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// s_waitcnt lgkmcnt(0): this wavefront's LDS reads have returned.
+__device__ __forceinline__ void wait_lgkmcnt0() {
+  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));
+}
+
+// Workgroup barrier without the memory fence __syncthreads() adds (which
+// would wait for every outstanding global load); the asm statements keep
+// the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void bare_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// LDS image of a tile row of RB bytes: chunk c of row r sits at chunk
+// c ^ f(r), f chosen so that the 16 rows one fragment-read pass serves (16
+// consecutive rows, one chunk index) land in 16 distinct 16-byte groups of
+// the 64 four-byte banks: with 128-byte rows two rows share the 256-byte
+// bank space, with 64-byte rows four do.
+template <int RB>
+__device__ __forceinline__ int swz_rb(int row, int c) {
+  if (RB == 128) return row * 128 + ((c ^ ((row >> 1) & 7)) << 4);
+  return row * 64 + ((c ^ ((row >> 2) & 3)) << 4);
+}
+
+// Plain-operand GEMM with direct global->LDS loads and a STAGES-deep ring
+// of LDS stages (each BM + BN rows of RB bytes, i.e. RB / sizeof(T) of k).
+// Every 1-KB group of rows is filled by one global_load_lds_dwordx4 of one
+// wavefront, lane l landing at byte 16 l of the group; the XOR swizzle is
+// applied on the source side (lane l fetches the logical chunk that belongs
+// at its physical slot), so the LDS image is the swizzled layout the
+// fragment reads expect. Loads run STAGES - 1 stages ahead of the MFMAs;
+// each wavefront waits only for its own loads of the stage it is about to
+// read (exact vmcnt), then a bare barrier publishes the stage. Rows past M
+// read row M - 1 (their results are never stored).
+template <typename T, typename TO, int BM, int BN, int WM, int WN, int RB, int STAGES, int EPI,
+          int OCC>
+__global__ void __launch_bounds__(WM * WN * 64, OCC) k_gemm_dl(GemmParams p) {
+  constexpr int NW = WM * WN;
+  constexpr int EPC = 16 / sizeof(T);
+  constexpr int BK = RB / sizeof(T);
+  constexpr int CPR = RB / 16;                 // chunks per row
+  constexpr int RPG = 1024 / RB;               // rows per 1-KB group
+  constexpr int WTM = BM / WM, WTN = BN / WN;
+  constexpr int MT = WTM / 32, NTL = WTN / 32;
+  static_assert(MT * 32 == WTM && NTL * 32 == WTN, "wave tile must be 32-aligned");
+  static_assert(EPI != EPI_GLU || (WTN % 64) == 0, "GLU pairs need 64-column wave tiles");
+  static_assert(BM % RPG == 0 && BN % RPG == 0, "whole groups");
+  constexpr int GROUPS = (BM + BN) / RPG;
+  static_assert(GROUPS % NW == 0, "groups spread evenly over wavefronts");
+  constexpr int GPW = GROUPS / NW;             // loads per wavefront per stage
+  static_assert(GPW * (STAGES - 2) < 64, "vmcnt range");
+  constexpr int STAGE = (BM + BN) * RB;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[STAGES * STAGE];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  // wavefront index as a scalar: LDS destinations (m0) then need no
+  // per-load readfirstlane
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WN, wn = wave % WN;
+  const int tiles_n = p.N / BN, tiles_m = (p.M + BM - 1) / BM;
+  int tm, tn;
+  tile_of<4>(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+
+  int seg = 0, nloc = n0;
+  if (EPI != EPI_GLU) {
+    seg = n0 / p.seg_n;
+    nloc = n0 - seg * p.seg_n;
+  }
+  const T* Ab = (const T*)p.A[seg];
+  const T* Bb = (const T*)p.Bm[seg];
+
+  const T* src[GPW];
 #pragma unroll
-    for (int i = 0; i < MT; ++i)
-#pragma unroll
-      for (int jp = 0; jp < NTL / 2; ++jp) {
-        const int col = (n0 + wn * WTN) / 2 + jp * 32 + cl;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int row = rbase + i * 32 + (v >> 2) * 8 + (v & 3);
-          const float a = clampf(acc[i][2 * jp][v], lo, hi);
-          const float b = clampf(acc[i][2 * jp + 1][v], lo, hi);
-          if (row < p.M) store_out(C, (size_t)row * p.ldc + col, a * sigmoidf_(b));
-        }
+  for (int i = 0; i < GPW; ++i) {
+    const int g = wave + i * NW;
+    const int r = g * RPG + lane / CPR;
+    const int pc = lane % CPR;
+    const int c = RB == 128 ? (pc ^ ((r >> 1) & 7)) : (pc ^ ((r >> 2) & 3));
+    if (r < BM) {
+      const int gm = min(m0 + r, p.M - 1);
+      src[i] = Ab + (size_t)gm * p.lda + c * EPC;
+    } else {
+      const int br = r - BM;
+      int wrow;
+      if (EPI == EPI_GLU) {
+        const int vr = n0 + br;
+        wrow = ((vr >> 5) & 1) * p.glu_d + (vr >> 6) * 32 + (vr & 31);
+      } else {
+        wrow = nloc + br;
       }
-  } else if (EPI == EPI_LNRELU) {
-    const float g = p.gain[cl];
-#pragma unroll
-    for (int i = 0; i < MT; ++i)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int row = rbase + i * 32 + (v >> 2) * 8 + (v & 3);
-        const float x = acc[i][0][v];
-        float s = x;
-#pragma unroll
-        for (int o = 16; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
-        const float mean = s * (1.0f / 32);
-        const float dx = x - mean;
-        float q = dx * dx;
-#pragma unroll
-        for (int o = 16; o > 0; o >>= 1) q += __shfl_xor(q, o, 64);
-        const float y = fmaxf(dx * rsqrtf(q * (1.0f / 32) + kEps) * g, 0.0f);
-        if (row < p.M) store_out(C, (size_t)row * p.ldc + cl, y);
-      }
-  } else {
-    const float lo = p.olo[seg], hi = p.ohi[seg];
-#pragma unroll
-    for (int j = 0; j < NTL; ++j) {
-      const int col = n0 + wn * WTN + j * 32 + cl;
-      const float sc = (EPI == EPI_STORE && p.colscale) ? p.colscale[col] : 1.0f;
-      const float bias = (EPI == EPI_BIAS) ? p.bias[col] : 0.0f;
-#pragma unroll
-      for (int i = 0; i < MT; ++i)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int row = rbase + i * 32 + (v >> 2) * 8 + (v & 3);
-          if (row >= p.M) continue;
-          const size_t idx = (size_t)row * p.ldc + col;
-          const float x = acc[i][j][v];
-          if (EPI == EPI_STORE) {
-            store_out(C, idx, clampf(x, lo, hi) * sc);
-          } else if (EPI == EPI_SILU) {
-            const float y = clampf(x, lo, hi);
-            store_out(C, idx, clampf(y * sigmoidf_(y), p.nlo, p.nhi));
-          } else if (EPI == EPI_RESID) {
-            float* H = (float*)p.C;
-            H[idx] += clampf(x, lo, hi);
-          } else if (EPI == EPI_BIAS) {
-            ((float*)p.C)[idx] = x + bias;
-          }
-        }
+      src[i] = Bb + (size_t)wrow * p.ldb + c * EPC;
     }
   }
+  auto issue = [&](int buf, int kt) {
+#pragma unroll
+    for (int i = 0; i < GPW; ++i) {
+      const int g = wave + i * NW;
+      __builtin_amdgcn_global_load_lds(
+          (const __attribute__((address_space(1))) void*)(src[i] + (size_t)kt * BK),
+          (__attribute__((address_space(3))) void*)(smem + buf * STAGE + g * 1024), 16, 0, 0);
+    }
+  };
+
+  f32x16 acc[MT][NTL];
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int j = 0; j < NTL; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+  // Fragments are double-buffered in registers: the reads of substep
+  // st + 1 (or of the next stage's substep 0) are issued before the MFMAs
+  // of substep st, and sched_barrier keeps the scheduler from sinking them
+  // back next to their use.
+  constexpr int NSUB = CPR / 2;
+  u32x4 fa[2][MT], fb[2][NTL];
+  auto load_frags = [&](int sel, const unsigned char* sb, int st) {
+    const int c = 2 * st + (lane >> 5);
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+      fa[sel][i] = *(const u32x4*)(sb + swz_rb<RB>(wm * WTM + i * 32 + (lane & 31), c));
+#pragma unroll
+    for (int j = 0; j < NTL; ++j)
+      fb[sel][j] = *(const u32x4*)(sb + BM * RB + swz_rb<RB>(wn * WTN + j * 32 + (lane & 31), c));
+  };
+
+  const int nk = p.K / BK;
+  // prologue: stages 0 .. STAGES-2 in flight, publish stage 0, queue the next
+#pragma unroll
+  for (int st = 0; st < STAGES - 1; ++st)
+    if (st < nk) issue(st, st);
+  if (STAGES - 2 < nk) wait_vmcnt<GPW * (STAGES - 2)>();
+  else wait_vmcnt<0>();
+  bare_barrier();
+  if (STAGES - 1 < nk) issue(STAGES - 1, STAGES - 1);
+  load_frags(0, smem, 0);
+
+  // One substep: the MFMAs on fragment set `cur`, with the operations the
+  // caller emitted just before threaded between them: after each of the
+  // first MFMAs one fragment read (for the next substep) and, in the
+  // publishing substep, one global->LDS load of a later stage. Issuing the
+  // loads back to back would stall the wavefront's issue for their whole
+  // duration; spread out, they hide under the MFMAs.
+  constexpr int NMFMA = MT * NTL, NLOAD = MT + NTL;
+  static_assert(NLOAD <= NMFMA, "interleave needs an MFMA per read");
+  auto mfmas = [&](int cur, int nreads, int nloads) {
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+      for (int j = 0; j < NTL; ++j) Mma<T>::run(acc[i][j], fb[cur][j], fa[cur][i]);
+    // reads and loads cannot pass each other (the compiler keeps LDS reads
+    // ahead of the LDS-writing loads), so: MFMA+read pairs, then MFMA+load
+    // pairs, then the remaining MFMAs (loads beyond the MFMA count go last)
+#pragma unroll
+    for (int q = 0; q < NMFMA; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+      if (q < nreads) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+      } else if (q < nreads + nloads) {
+        __builtin_amdgcn_sched_group_barrier(0x004, 1, 0);  // scalar setup
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one global->LDS load
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // Every iteration but the last publishes the next stage before its last
+  // substep; the last iteration is peeled so the loop body has no branch.
+  for (int kt = 0; kt + 1 < nk; ++kt) {
+    const unsigned char* sb = smem + (kt % STAGES) * STAGE;
+#pragma unroll
+    for (int st = 0; st < NSUB; ++st) {
+      const int cur = st & 1;
+      if (st + 1 < NSUB) {
+        load_frags(cur ^ 1, sb, st + 1);
+      } else {
+        // Publish stage kt + 1 (this wave's loads of it have landed and its
+        // reads of stage kt have returned), start reading it, and refill
+        // stage kt's buffer with stage kt + STAGES. Near the end there is no
+        // such stage; the buffer then gets the last stage again (valid
+        // addresses, never read: the stages still to come live in the other
+        // buffers), which keeps this substep free of branches so its loads
+        // can interleave with the MFMAs. The reads go first: the compiler
+        // cannot tell the two buffers apart and would keep them in order.
+        if (kt + STAGES - 1 < nk) wait_vmcnt<GPW * (STAGES - 2)>();
+        else wait_vmcnt<0>();
+        wait_lgkmcnt0();
+        bare_barrier();
+        load_frags(cur ^ 1, smem + ((kt + 1) % STAGES) * STAGE, 0);
+        issue(kt % STAGES, min(kt + STAGES, nk - 1));
+        mfmas(cur, NLOAD, GPW);
+        continue;
+      }
+      mfmas(cur, NLOAD, 0);
+    }
+  }
+  {
+    const unsigned char* sb = smem + ((nk - 1) % STAGES) * STAGE;
+#pragma unroll
+    for (int st = 0; st < NSUB; ++st) {
+      const int cur = st & 1;
+      if (st + 1 < NSUB) load_frags(cur ^ 1, sb, st + 1);
+      mfmas(cur, st + 1 < NSUB ? NLOAD : 0, 0);
+    }
+  }
+  epilogue<TO, MT, NTL, EPI>(p, acc, m0 + wm * WTM, n0 + wn * WTN, seg, lane);
+}
+
+template <typename T, typename TO, int BM, int BN, int WM, int WN, int RB, int STAGES, int EPI,
+          int OCC = 1>
+hipError_t run_dl(const GemmParams& p, hipStream_t s) {
+  if (p.M <= 0) return hipSuccess;
+  const int tiles = ((p.M + BM - 1) / BM) * (p.N / BN);
+  hipLaunchKernelGGL((k_gemm_dl<T, TO, BM, BN, WM, WN, RB, STAGES, EPI, OCC>), dim3(tiles),
+                     dim3(WM * WN * 64), 0, s, p);
+  return hipGetLastError();
 }
 
 template <typename T, typename TO, int BM, int BN, int WM, int WN, int AL, int EPI>
@@ -271,25 +564,48 @@ hipError_t run(const GemmParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <typename T>
-hipError_t dispatch(int epi, int aload, bool out_bf16, const GemmParams& p, hipStream_t s) {
-  typedef typename std::conditional<std::is_same<T, float>::value, float, bf16>::type TB;
-  if (aload == A_CONV1) {
-    if (out_bf16) return run<T, TB, 128, 32, 4, 1, A_CONV1, EPI_LNRELU>(p, s);
-    return run<T, float, 128, 32, 4, 1, A_CONV1, EPI_LNRELU>(p, s);
+// fp32 operands (the parity path): register-staged 128x128 tiles.
+hipError_t dispatch_f32(int epi, int aload, const GemmParams& p, hipStream_t s) {
+  if (aload == A_CONV1) return run<float, float, 128, 32, 4, 1, A_CONV1, EPI_LNRELU>(p, s);
+  switch (epi) {
+    case EPI_STORE: return run<float, float, 128, 128, 2, 2, A_PLAIN, EPI_STORE>(p, s);
+    case EPI_SILU: return run<float, float, 128, 128, 2, 2, A_PLAIN, EPI_SILU>(p, s);
+    case EPI_GLU: return run<float, float, 128, 128, 2, 2, A_PLAIN, EPI_GLU>(p, s);
+    case EPI_RESID: return run<float, float, 128, 128, 2, 2, A_PLAIN, EPI_RESID>(p, s);
+    case EPI_BIAS: return run<float, float, 128, 128, 2, 2, A_PLAIN, EPI_BIAS>(p, s);
   }
+  return hipErrorInvalidValue;
+}
+
+// bf16 operands: direct-to-LDS pipelined kernels; the tile shape follows
+// the output width (tiles per wave of 256 CUs) and the depth of K.
+//  wide   (N % 256 == 0, N >= 2048): 256x256, 8 wavefronts of 128x64
+//  deep   (K >= 2048, N % 256 == 0): 192x256, 4 wavefronts of 96x128
+//  narrow (otherwise):               256x128, 8 wavefronts of 64x64, two blocks per CU
+template <int EPI, typename TO>
+hipError_t run_bf16(const GemmParams& p, hipStream_t s) {
+  if (p.N % 256 == 0 && p.N >= 2048)
+    return run_dl<bf16, TO, 256, 256, 2, 4, 64, 4, EPI>(p, s);
+  if (p.K >= 2048 && p.N % 256 == 0)
+    return run_dl<bf16, TO, 192, 256, 2, 2, 64, 3, EPI, 2>(p, s);
+  return run_dl<bf16, TO, 256, 128, 4, 2, 64, 3, EPI, 2>(p, s);
+}
+
+hipError_t dispatch_bf16(int epi, int aload, bool out_bf16, const GemmParams& p, hipStream_t s) {
+  if (aload == A_CONV1) {
+    if (out_bf16) return run<bf16, bf16, 128, 32, 4, 1, A_CONV1, EPI_LNRELU>(p, s);
+    return run<bf16, float, 128, 32, 4, 1, A_CONV1, EPI_LNRELU>(p, s);
+  }
+  if (p.N % 128 != 0) return hipErrorInvalidValue;
   switch (epi) {
     case EPI_STORE:
-      if (out_bf16) return run<T, TB, 128, 128, 2, 2, A_PLAIN, EPI_STORE>(p, s);
-      return run<T, float, 128, 128, 2, 2, A_PLAIN, EPI_STORE>(p, s);
+      return out_bf16 ? run_bf16<EPI_STORE, bf16>(p, s) : run_bf16<EPI_STORE, float>(p, s);
     case EPI_SILU:
-      if (out_bf16) return run<T, TB, 128, 128, 2, 2, A_PLAIN, EPI_SILU>(p, s);
-      return run<T, float, 128, 128, 2, 2, A_PLAIN, EPI_SILU>(p, s);
+      return out_bf16 ? run_bf16<EPI_SILU, bf16>(p, s) : run_bf16<EPI_SILU, float>(p, s);
     case EPI_GLU:
-      if (out_bf16) return run<T, TB, 128, 128, 2, 2, A_PLAIN, EPI_GLU>(p, s);
-      return run<T, float, 128, 128, 2, 2, A_PLAIN, EPI_GLU>(p, s);
-    case EPI_RESID: return run<T, float, 128, 128, 2, 2, A_PLAIN, EPI_RESID>(p, s);
-    case EPI_BIAS: return run<T, float, 128, 128, 2, 2, A_PLAIN, EPI_BIAS>(p, s);
+      return out_bf16 ? run_bf16<EPI_GLU, bf16>(p, s) : run_bf16<EPI_GLU, float>(p, s);
+    case EPI_RESID: return run_bf16<EPI_RESID, float>(p, s);
+    case EPI_BIAS: return run_bf16<EPI_BIAS, float>(p, s);
   }
   return hipErrorInvalidValue;
 }
@@ -298,8 +614,8 @@ hipError_t dispatch(int epi, int aload, bool out_bf16, const GemmParams& p, hipS
 
 hipError_t launch_gemm(ae_dtype dt, int epi, int aload, bool out_bf16, const GemmParams& p,
                        hipStream_t s) {
-  if (dt == AE_BF16) return dispatch<bf16>(epi, aload, out_bf16, p, s);
-  return dispatch<float>(epi, aload, false, p, s);
+  if (dt == AE_BF16) return dispatch_bf16(epi, aload, out_bf16, p, s);
+  return dispatch_f32(epi, aload, p, s);
 }
 
 }  // namespace ae

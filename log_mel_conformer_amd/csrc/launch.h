@@ -58,8 +58,8 @@ hipError_t launch_conv0(ae_dtype dt, const float* mel, const int64_t* frame_off,
                         const float* g0, void* y0, hipStream_t s);
 
 // -------------------------------------------------------------- row norms
-// For each row of h [n][d]:
-//   if y:     h += scale * rms(y) * w_post
+// For each row of h [n][d] (float):
+//   if y:     h += scale * rms(y) * w_post   (y [n][d] in dtype dt)
 //   if w_out: h  = rms(h) * w_out
 //   store h (when y or w_out was applied); if h_copy: also h as dtype dt
 //   if w_next: a_i = clamp(rms(h) * w_next, lo_i, hi_i) for i < n_out (dtype dt)
@@ -68,7 +68,7 @@ struct RowNormParams {
   int64_t n;
   int d;
   float* h;
-  const float* y;
+  const void* y;
   float scale;
   const float* w_post;
   const float* w_out;
@@ -89,8 +89,9 @@ hipError_t launch_attention(ae_dtype dt, const void* qkv, const float* R, const 
                             float hi, void* o, hipStream_t s);
 
 // ------------------------------------------------------------ light conv
-// u [n][d] (dt) -> c = clamp(silu(rms(dwconv(u)) * w_norm), lo, hi) (dt)
-hipError_t launch_lconv(ae_dtype dt, const void* u, const float* w_dw, int kernel,
+// u [n][d] (dt) -> c = clamp(silu(rms(dwconv(u)) * w_norm), lo, hi) (dt);
+// w_dwt: the depthwise taps transposed, [kernel][d].
+hipError_t launch_lconv(ae_dtype dt, const void* u, const float* w_dwt, int kernel,
                         const float* w_norm, const int32_t* pos, int64_t n, int d, float lo,
                         float hi, void* c, hipStream_t s);
 
@@ -107,5 +108,7 @@ hipError_t launch_relative_keys(ae_dtype dt, const void* rel_k, int d, int n_dis
 hipError_t launch_qkv_scale(const float* pds, int d, int head_dim, float q_scale, float k_scale,
                             float* colscale, hipStream_t s);
 hipError_t launch_conv1_reorder(ae_dtype dt, const void* w1, void* w1r, hipStream_t s);
+// [d][K] -> [K][d]
+hipError_t launch_transpose_taps(const float* w, int d, int K, float* wt, hipStream_t s);
 
 }  // namespace ae

@@ -4,17 +4,37 @@
 // GEMM epilogue.
 //
 // out[t, c] = sum_k w[c][k] u[t - (K-1-k), c], skipping taps that reach
-// before the clip start (K-1-k > pos[t]). One wavefront per row, a lane
-// holding d/64 channels; the K rows a token reads are its own and its
-// K-1 predecessors, which neighbouring wavefronts read too, so they come
-// from cache after the first touch.
+// before the clip start (K-1-k > pos[t]). The taps arrive transposed,
+// wt[k][c], so a lane reads four channels of one tap as one float4. One
+// wavefront per row, a lane holding d/64 channels (four runs of four); the
+// K rows a token reads are its own and its K-1 predecessors, which
+// neighbouring wavefronts read too, so they come from cache after the
+// first touch.
 #include "launch.h"
 
 namespace ae {
 namespace {
 
+__device__ __forceinline__ void load4(const float* p, float* v) {
+  const float4 a = *(const float4*)p;
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+}
+__device__ __forceinline__ void load4(const bf16* p, float* v) {
+  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+  const bf16x4 a = *(const bf16x4*)p;
+  v[0] = (float)a[0]; v[1] = (float)a[1]; v[2] = (float)a[2]; v[3] = (float)a[3];
+}
+__device__ __forceinline__ void store4v(float* p, const float* v) {
+  *(float4*)p = make_float4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ void store4v(bf16* p, const float* v) {
+  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+  const bf16x4 a = {(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
+  *(bf16x4*)p = a;
+}
+
 template <typename T, int VPL>
-__global__ void __launch_bounds__(256) k_lconv(const T* __restrict__ u, const float* __restrict__ wdw,
+__global__ void __launch_bounds__(256) k_lconv(const T* __restrict__ u, const float* __restrict__ wt,
                                                int K, const float* __restrict__ wn,
                                                const int32_t* __restrict__ pos, int64_t n, float lo,
                                                float hi, T* __restrict__ out) {
@@ -29,15 +49,19 @@ __global__ void __launch_bounds__(256) k_lconv(const T* __restrict__ u, const fl
   for (int i = 0; i < VPL; ++i) x[i] = 0.f;
   for (int k = 0; k < K; ++k) {
     const int back = K - 1 - k;
-    if (back > pr || back > row) continue;  // never before the packed buffer
+    if (back > pr || back > row) continue;  // never before the clip or the buffer
     const T* ur = u + (row - back) * d;
 #pragma unroll
-    for (int q = 0; q < NV; ++q)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int c = q * 256 + lane * 4 + e;
-        x[4 * q + e] += wdw[c * K + k] * to_f32(ur[c]);
-      }
+    for (int q = 0; q < NV; ++q) {
+      const int c = q * 256 + lane * 4;
+      const float4 w = *(const float4*)(wt + k * d + c);
+      float uv[4];
+      load4(ur + c, uv);
+      x[4 * q] += w.x * uv[0];
+      x[4 * q + 1] += w.y * uv[1];
+      x[4 * q + 2] += w.z * uv[2];
+      x[4 * q + 3] += w.w * uv[3];
+    }
   }
   float ss = 0.f;
 #pragma unroll
@@ -45,28 +69,33 @@ __global__ void __launch_bounds__(256) k_lconv(const T* __restrict__ u, const fl
   const float inv = rsqrtf(wave_sum(ss) * (1.0f / d) + kEps);
   T* orow = out + row * d;
 #pragma unroll
-  for (int q = 0; q < NV; ++q)
+  for (int q = 0; q < NV; ++q) {
+    const int c = q * 256 + lane * 4;
+    const float4 g = *(const float4*)(wn + c);
+    const float gg[4] = {g.x, g.y, g.z, g.w};
+    float o[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int c = q * 256 + lane * 4 + e;
-      const float y = x[4 * q + e] * inv * wn[c];
-      orow[c] = from_f32<T>(clampf(y * sigmoidf_(y), lo, hi));
+      const float y = x[4 * q + e] * inv * gg[e];
+      o[e] = clampf(y * sigmoidf_(y), lo, hi);
     }
+    store4v(orow + c, o);
+  }
 }
 
 }  // namespace
 
-hipError_t launch_lconv(ae_dtype dt, const void* u, const float* w_dw, int kernel,
+hipError_t launch_lconv(ae_dtype dt, const void* u, const float* w_dwt, int kernel,
                         const float* w_norm, const int32_t* pos, int64_t n, int d, float lo,
                         float hi, void* c, hipStream_t s) {
   if (n <= 0) return hipSuccess;
   if (d != 1024) return hipErrorInvalidValue;
   const unsigned grid = (unsigned)((n + 3) / 4);
   if (dt == AE_BF16)
-    hipLaunchKernelGGL((k_lconv<bf16, 16>), dim3(grid), dim3(256), 0, s, (const bf16*)u, w_dw,
+    hipLaunchKernelGGL((k_lconv<bf16, 16>), dim3(grid), dim3(256), 0, s, (const bf16*)u, w_dwt,
                        kernel, w_norm, pos, n, lo, hi, (bf16*)c);
   else
-    hipLaunchKernelGGL((k_lconv<float, 16>), dim3(grid), dim3(256), 0, s, (const float*)u, w_dw,
+    hipLaunchKernelGGL((k_lconv<float, 16>), dim3(grid), dim3(256), 0, s, (const float*)u, w_dwt,
                        kernel, w_norm, pos, n, lo, hi, (float*)c);
   return hipGetLastError();
 }

@@ -14,6 +14,23 @@
 namespace ae {
 namespace {
 
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void load4(const float* p, float* v) {
+  const float4 a = *(const float4*)p;
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+}
+__device__ __forceinline__ void load4(const bf16* p, float* v) {
+  const bf16x4 a = *(const bf16x4*)p;
+  v[0] = (float)a[0]; v[1] = (float)a[1]; v[2] = (float)a[2]; v[3] = (float)a[3];
+}
+__device__ __forceinline__ void store4v(float* p, const float* v) {
+  *(float4*)p = make_float4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ void store4v(bf16* p, const float* v) {
+  const bf16x4 a = {(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
+  *(bf16x4*)p = a;
+}
+
 template <typename T, int VPL>
 __global__ void __launch_bounds__(256) k_rownorm(RowNormParams p) {
   constexpr int NV = VPL / 4;
@@ -31,13 +48,10 @@ __global__ void __launch_bounds__(256) k_rownorm(RowNormParams p) {
   }
   if (p.y) {
     float y[VPL];
-    const float* yrow = p.y + row * d;
+    const T* yrow = (const T*)p.y + row * d;
     float ss = 0.f;
 #pragma unroll
-    for (int q = 0; q < NV; ++q) {
-      const float4 v = *(const float4*)(yrow + q * 256 + lane * 4);
-      y[4 * q] = v.x; y[4 * q + 1] = v.y; y[4 * q + 2] = v.z; y[4 * q + 3] = v.w;
-    }
+    for (int q = 0; q < NV; ++q) load4(yrow + q * 256 + lane * 4, y + 4 * q);
 #pragma unroll
     for (int i = 0; i < VPL; ++i) ss += y[i] * y[i];
     const float inv = rsqrtf(wave_sum(ss) * invd + kEps);
@@ -71,7 +85,7 @@ __global__ void __launch_bounds__(256) k_rownorm(RowNormParams p) {
   if (p.h_copy) {
     T* crow = (T*)p.h_copy + row * d;
 #pragma unroll
-    for (int i = 0; i < VPL; ++i) crow[(i >> 2) * 256 + lane * 4 + (i & 3)] = from_f32<T>(x[i]);
+    for (int q = 0; q < NV; ++q) store4v(crow + q * 256 + lane * 4, x + 4 * q);
   }
   if (p.w_next || p.plain_next) {
     float ss = 0.f;
@@ -89,10 +103,12 @@ __global__ void __launch_bounds__(256) k_rownorm(RowNormParams p) {
       T* arow = (T*)p.a[s] + row * d;
       const float lo = p.lo[s], hi = p.hi[s];
 #pragma unroll
-      for (int q = 0; q < NV; ++q)
+      for (int q = 0; q < NV; ++q) {
+        float v[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          arow[q * 256 + lane * 4 + e] = from_f32<T>(clampf(x[4 * q + e], lo, hi));
+        for (int e = 0; e < 4; ++e) v[e] = clampf(x[4 * q + e], lo, hi);
+        store4v(arow + q * 256 + lane * 4, v);
+      }
     }
   }
 }
