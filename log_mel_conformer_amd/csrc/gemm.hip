@@ -371,7 +371,7 @@ __device__ __forceinline__ int swz_rb(int row, int c) {
 // read (exact vmcnt), then a bare barrier publishes the stage. Rows past M
 // read row M - 1 (their results are never stored).
 template <typename T, typename TO, int BM, int BN, int WM, int WN, int RB, int STAGES, int EPI,
-          int OCC>
+          int OCC, int GM>
 __global__ void __launch_bounds__(WM * WN * 64, OCC) k_gemm_dl(GemmParams p) {
   constexpr int NW = WM * WN;
   constexpr int EPC = 16 / sizeof(T);
@@ -397,7 +397,7 @@ __global__ void __launch_bounds__(WM * WN * 64, OCC) k_gemm_dl(GemmParams p) {
   const int wm = wave / WN, wn = wave % WN;
   const int tiles_n = p.N / BN, tiles_m = (p.M + BM - 1) / BM;
   int tm, tn;
-  tile_of<4>(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
+  tile_of<GM>(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
 
   int seg = 0, nloc = n0;
@@ -546,11 +546,11 @@ __global__ void __launch_bounds__(WM * WN * 64, OCC) k_gemm_dl(GemmParams p) {
 }
 
 template <typename T, typename TO, int BM, int BN, int WM, int WN, int RB, int STAGES, int EPI,
-          int OCC = 1>
+          int OCC = 1, int GM = 4>
 hipError_t run_dl(const GemmParams& p, hipStream_t s) {
   if (p.M <= 0) return hipSuccess;
   const int tiles = ((p.M + BM - 1) / BM) * (p.N / BN);
-  hipLaunchKernelGGL((k_gemm_dl<T, TO, BM, BN, WM, WN, RB, STAGES, EPI, OCC>), dim3(tiles),
+  hipLaunchKernelGGL((k_gemm_dl<T, TO, BM, BN, WM, WN, RB, STAGES, EPI, OCC, GM>), dim3(tiles),
                      dim3(WM * WN * 64), 0, s, p);
   return hipGetLastError();
 }
@@ -579,13 +579,13 @@ hipError_t dispatch_f32(int epi, int aload, const GemmParams& p, hipStream_t s) 
 
 // bf16 operands: direct-to-LDS pipelined kernels; the tile shape follows
 // the output width (tiles per wave of 256 CUs) and the depth of K.
-//  wide   (N % 256 == 0, N >= 2048): 256x256, 8 wavefronts of 128x64
+//  wide   (N % 256 == 0, N >= 2048): 256x256, 8 wavefronts of 128x64, two 128-byte stages
 //  deep   (K >= 2048, N % 256 == 0): 192x256, 4 wavefronts of 96x128
 //  narrow (otherwise):               256x128, 8 wavefronts of 64x64, two blocks per CU
 template <int EPI, typename TO>
 hipError_t run_bf16(const GemmParams& p, hipStream_t s) {
   if (p.N % 256 == 0 && p.N >= 2048)
-    return run_dl<bf16, TO, 256, 256, 2, 4, 64, 4, EPI>(p, s);
+    return run_dl<bf16, TO, 256, 256, 2, 4, 128, 2, EPI>(p, s);
   if (p.K >= 2048 && p.N % 256 == 0)
     return run_dl<bf16, TO, 192, 256, 2, 2, 64, 3, EPI, 2>(p, s);
   return run_dl<bf16, TO, 256, 128, 4, 2, 64, 3, EPI, 2>(p, s);

@@ -2,17 +2,20 @@
 // magnitude, 128 HTK mel bands, natural log (egemma2_audio.rs, module
 // documentation step 2, mel_filter_bank and MelFrontend::log_mel).
 //
-// One wavefront per frame. The 512-point real FFT is a 256-point complex
-// FFT of z[n] = x[2n] + i x[2n+1]: four radix-4 Stockham stages, one
-// butterfly per lane per stage (256 = 4 x 64), ping-ponging through LDS,
-// then the even/odd split X[k] = E[k] + e^{-2 pi i k/512} O[k]. The first
-// stage reads its four inputs straight from the waveform (the window is
-// applied on the way), so a frame costs one pass over 320 samples; frames
-// of one block overlap by half and share the cache lines. The mel bank
-// has at most two nonzero weights per bin (506 in all), so each band is a
-// short contiguous dot product over its own bins, not a dense 257x128
-// product. Tables (window, twiddles, bands) are computed on the host in
-// double and rounded to float once.
+// Sixteen lanes per frame, four frames per wavefront. The 512-point real
+// FFT is a 256-point complex FFT of z[n] = x[2n] + i x[2n+1] (the last 96
+// z are zero: the frame is 320 samples), split as 256 = 16 x 16: lane j
+// first takes the 16-point DFT over z[16 m + j] in registers, multiplies by
+// e^{-2 pi i j k / 256}, and the wavefront transposes through LDS; lane j
+// then takes the 16-point DFT over the other index and holds Z[j + 16 k].
+// The real spectrum follows from X[k] = E[k] + e^{-2 pi i k / 512} O[k] with
+// E, O formed from Z[k] and Z[256 - k] (the partner read from LDS). Each
+// 16-point DFT is radix 4 x 4 with constant twiddles. The mel bank has at
+// most two nonzero weights per bin (506 in all), so each band is a short
+// contiguous dot product over its own bins; lane j takes bands j, j + 16,
+// ..., which spreads narrow and wide bands evenly over the lanes. All
+// exchanges stay inside a wavefront. Window, twiddle and band tables are
+// computed on the host in double, rounded to float once, and staged in LDS.
 #include <math.h>
 
 #include <mutex>
@@ -24,10 +27,12 @@ namespace ae {
 namespace {
 
 constexpr int kMaxBandW = 640;
+constexpr int FPB = 16;        // frames per block (4 per wavefront)
 
 struct MelTables {
   float hann[kFrame];
-  float2 tw[kFft];          // exp(-2 pi i m / 512)
+  float2 tw256[256];        // exp(-2 pi i m / 256)
+  float2 tw512[256];        // exp(-2 pi i m / 512), m < 256
   int band_start[kMels];
   int band_count[kMels];
   int band_woff[kMels];
@@ -48,9 +53,10 @@ std::vector<double> linspace_d(double a, double b, int n) {
 bool build_tables(MelTables* t) {
   for (int n = 0; n < kFrame; ++n)
     t->hann[n] = (float)(0.5 - 0.5 * cos(2.0 * M_PI * n / kFrame));
-  for (int m = 0; m < kFft; ++m) {
-    const double a = -2.0 * M_PI * m / kFft;
-    t->tw[m] = make_float2((float)cos(a), (float)sin(a));
+  for (int m = 0; m < 256; ++m) {
+    const double a = -2.0 * M_PI * m / 256.0, b = -2.0 * M_PI * m / 512.0;
+    t->tw256[m] = make_float2((float)cos(a), (float)sin(a));
+    t->tw512[m] = make_float2((float)cos(b), (float)sin(b));
   }
   // HTK mel scale, 130 edges over 0..8 kHz, triangles on 257 bins, no norm.
   auto hz2mel = [](double f) { return 2595.0 * log10(1.0 + f / 700.0); };
@@ -85,91 +91,218 @@ bool build_tables(MelTables* t) {
 __device__ __forceinline__ float2 cmul(float2 a, float2 b) {
   return make_float2(a.x * b.x - a.y * b.y, a.x * b.y + a.y * b.x);
 }
+__device__ __forceinline__ float2 cadd(float2 a, float2 b) { return make_float2(a.x + b.x, a.y + b.y); }
+__device__ __forceinline__ float2 csub(float2 a, float2 b) { return make_float2(a.x - b.x, a.y - b.y); }
+// a * (-i)
+__device__ __forceinline__ float2 mul_mi(float2 a) { return make_float2(a.y, -a.x); }
 
-// 4 frames per 256-thread block, one per wavefront; grid-stride over frames.
+// y_k = sum_m a_m (-i)^{mk}
+__device__ __forceinline__ void dft4(float2& a0, float2& a1, float2& a2, float2& a3) {
+  const float2 s02 = cadd(a0, a2), d02 = csub(a0, a2);
+  const float2 s13 = cadd(a1, a3), d13 = mul_mi(csub(a1, a3));
+  a0 = cadd(s02, s13);
+  a1 = cadd(d02, d13);
+  a2 = csub(s02, s13);
+  a3 = csub(d02, d13);
+}
+
+// e^{-2 pi i e / 16} for e = 0..15 (cos and sin of multiples of pi/8).
+__device__ __forceinline__ float2 w16(int e) {
+  constexpr float c1 = 0.92387953251128675613f, s1 = 0.38268343236508977173f;
+  constexpr float r2 = 0.70710678118654752440f;
+  switch (e & 15) {
+    case 0: return make_float2(1.f, 0.f);
+    case 1: return make_float2(c1, -s1);
+    case 2: return make_float2(r2, -r2);
+    case 3: return make_float2(s1, -c1);
+    case 4: return make_float2(0.f, -1.f);
+    case 6: return make_float2(-r2, -r2);
+    case 9: return make_float2(-c1, s1);
+    default: return make_float2(0.f, 0.f);  // not used by dft16
+  }
+}
+
+// 16-point DFT in place: input index m = 4 m1 + m2, output k = k1 + 4 k2.
+__device__ __forceinline__ void dft16(float2 (&x)[16]) {
+#pragma unroll
+  for (int m2 = 0; m2 < 4; ++m2) dft4(x[m2], x[4 + m2], x[8 + m2], x[12 + m2]);
+  // x[4 k1 + m2] now holds A[m2][k1]; twiddle by W16^(m2 k1)
+#pragma unroll
+  for (int m2 = 1; m2 < 4; ++m2)
+#pragma unroll
+    for (int k1 = 1; k1 < 4; ++k1) x[4 * k1 + m2] = cmul(x[4 * k1 + m2], w16(m2 * k1));
+  float2 y[16];
+#pragma unroll
+  for (int k1 = 0; k1 < 4; ++k1) {
+    float2 a0 = x[4 * k1], a1 = x[4 * k1 + 1], a2 = x[4 * k1 + 2], a3 = x[4 * k1 + 3];
+    dft4(a0, a1, a2, a3);
+    y[k1] = a0;
+    y[k1 + 4] = a1;
+    y[k1 + 8] = a2;
+    y[k1 + 12] = a3;
+  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) x[i] = y[i];
+}
+
+// Wave-local LDS hand-off: this wavefront's LDS writes are visible to its
+// own later reads.
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+constexpr int TLD = 17;    // transpose row stride (float2)
+constexpr int MAXB_LDS = 512;  // clips whose offsets are staged in LDS
+
+// Largest c with off[c] <= r over off[0..B] held in LDS.
+__device__ __forceinline__ int find_clip_lds(const int64_t* off, int B, int64_t r) {
+  int lo = 0, hi = B - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (off[mid] <= r) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
 __global__ void __launch_bounds__(256) k_logmel(const float* __restrict__ wave,
                                                 const int64_t* __restrict__ sample_off,
                                                 const int64_t* __restrict__ frame_off, int B,
                                                 int64_t total, float* __restrict__ mel) {
-  __shared__ float2 buf[4][2][256];
-  __shared__ float mag[4][260];
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  for (int64_t g0 = (int64_t)blockIdx.x * 4; g0 < total; g0 += (int64_t)gridDim.x * 4) {
-    const int64_t g = g0 + w;
+  __shared__ float2 tw256[256];
+  __shared__ float2 tw512[256];
+  __shared__ float hann[kFrame];
+  __shared__ int bstart[kMels], bcount[kMels], bwoff[kMels];
+  __shared__ float bw[kMaxBandW];
+  __shared__ int64_t soff[MAXB_LDS + 1], foff[MAXB_LDS + 1];
+  // per frame: transpose buffer, then Z in natural order, then magnitudes,
+  // then the 128 outputs
+  __shared__ __attribute__((aligned(16))) float2 xbuf[FPB][16 * TLD];
+  for (int i = threadIdx.x; i < 256; i += 256) {
+    tw256[i] = g_mel.tw256[i];
+    tw512[i] = g_mel.tw512[i];
+  }
+  for (int i = threadIdx.x; i < kFrame; i += 256) hann[i] = g_mel.hann[i];
+  for (int i = threadIdx.x; i < kMels; i += 256) {
+    bstart[i] = g_mel.band_start[i];
+    bcount[i] = g_mel.band_count[i];
+    bwoff[i] = g_mel.band_woff[i];
+  }
+  for (int i = threadIdx.x; i < kMaxBandW; i += 256) bw[i] = g_mel.band_w[i];
+  const bool lds_off = B <= MAXB_LDS;
+  if (lds_off)
+    for (int i = threadIdx.x; i <= B; i += 256) {
+      soff[i] = sample_off[i];
+      foff[i] = frame_off[i];
+    }
+  __syncthreads();
+
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int fl = wv * 4 + (lane >> 4);   // frame slot in the block
+  const int j = lane & 15;
+  float2* T = xbuf[fl];
+  float* M = (float*)xbuf[fl];            // magnitudes, after the split
+  // Raw samples of the frame group a block handles next: loaded one group
+  // ahead (register double buffer), branch-free: an address outside the
+  // clip is clamped to a valid one and its window weight set to zero.
+  float xr[20], wr[20];
+  auto fetch = [&](int64_t g0) {
+    const int64_t g = g0 + fl;
     const bool active = g < total;
     int64_t base = 0, start = 0;
     if (active) {
-      const int c = find_clip(frame_off, B, g);
-      start = sample_off[c];
-      base = start + (g - frame_off[c]) * kHop - kHop;  // frame starts 160 samples early
-    }
-    // stage 0 inputs: z[lane + 64 r] = x[2n] + i x[2n+1], n < 160 nonzero
-    float2 v[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int n = lane + 64 * r;
-      float x0 = 0.f, x1 = 0.f;
-      if (active && n < kFrame / 2) {
-        const int64_t s0 = base + 2 * n;
-        if (s0 >= start) x0 = wave[s0] * g_mel.hann[2 * n];
-        if (s0 + 1 >= start) x1 = wave[s0 + 1] * g_mel.hann[2 * n + 1];
+      int c;
+      if (lds_off) {
+        c = find_clip_lds(foff, B, g);
+        start = soff[c];
+        base = start + (g - foff[c]) * kHop - kHop;  // frame starts 160 samples early
+      } else {
+        c = find_clip(frame_off, B, g);
+        start = sample_off[c];
+        base = start + (g - frame_off[c]) * kHop - kHop;
       }
-      v[r] = make_float2(x0, x1);
     }
-    // four radix-4 Stockham stages (autosort: natural order out)
-    int dst = 0;
 #pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      const int Ns = 1 << (2 * st);
-      if (st > 0) {
+    for (int m = 0; m < 10; ++m) {
+      const int n = 16 * m + j;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) v[r] = buf[w][dst ^ 1][lane + 64 * r];
+      for (int e = 0; e < 2; ++e) {
+        const int64_t sidx = base + 2 * n + e;
+        const bool ok = active && sidx >= start;
+        xr[2 * m + e] = wave[ok ? sidx : 0];
+        wr[2 * m + e] = ok ? hann[2 * n + e] : 0.f;
       }
-      const int k = lane & (Ns - 1);
-      const int step = 128 >> (2 * st);  // 512 / (4 Ns)
-#pragma unroll
-      for (int r = 1; r < 4; ++r) v[r] = cmul(v[r], g_mel.tw[(r * k * step) & 511]);
-      const float2 s02 = make_float2(v[0].x + v[2].x, v[0].y + v[2].y);
-      const float2 d02 = make_float2(v[0].x - v[2].x, v[0].y - v[2].y);
-      const float2 s13 = make_float2(v[1].x + v[3].x, v[1].y + v[3].y);
-      const float2 d13 = make_float2(v[1].x - v[3].x, v[1].y - v[3].y);
-      // y1 = d02 - i d13, y3 = d02 + i d13
-      const float2 y0 = make_float2(s02.x + s13.x, s02.y + s13.y);
-      const float2 y1 = make_float2(d02.x + d13.y, d02.y - d13.x);
-      const float2 y2 = make_float2(s02.x - s13.x, s02.y - s13.y);
-      const float2 y3 = make_float2(d02.x - d13.y, d02.y + d13.x);
-      const int idx = (lane / Ns) * Ns * 4 + k;
-      buf[w][dst][idx] = y0;
-      buf[w][dst][idx + Ns] = y1;
-      buf[w][dst][idx + 2 * Ns] = y2;
-      buf[w][dst][idx + 3 * Ns] = y3;
-      __syncthreads();
-      dst ^= 1;
     }
-    const float2* Z = buf[w][dst ^ 1];
-    // real split: X[k] = E[k] + e^{-2 pi i k / 512} O[k]
+  };
+  int64_t g0 = (int64_t)blockIdx.x * FPB;
+  if (g0 < total) fetch(g0);
+  for (; g0 < total; g0 += (int64_t)gridDim.x * FPB) {
+    const int64_t g = g0 + fl;
+    const bool active = g < total;
+    // pass 1: lane j = n2, DFT over m of z[16 m + j]; z is zero for m >= 10
+    float2 x[16];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int k = lane + 64 * r;
-      const float2 zk = Z[k], zn = Z[(256 - k) & 255];
+    for (int m = 0; m < 16; ++m)
+      x[m] = m < 10 ? make_float2(xr[2 * m] * wr[2 * m], xr[2 * m + 1] * wr[2 * m + 1])
+                    : make_float2(0.f, 0.f);
+    const int64_t g1 = g0 + (int64_t)gridDim.x * FPB;
+    if (g1 < total) fetch(g1);
+    dft16(x);
+#pragma unroll
+    for (int k1 = 0; k1 < 16; ++k1) {
+      const float2 t = k1 == 0 ? x[0] : cmul(x[k1], tw256[(j * k1) & 255]);
+      T[k1 * TLD + j] = t;
+    }
+    wave_sync();
+    // pass 2: lane j = k1, DFT over n2
+#pragma unroll
+    for (int n2 = 0; n2 < 16; ++n2) x[n2] = T[j * TLD + n2];
+    dft16(x);                       // x[k2] = Z[j + 16 k2]
+    wave_sync();
+#pragma unroll
+    for (int k2 = 0; k2 < 16; ++k2) T[j + 16 * k2] = x[k2];
+    wave_sync();
+    // real split and magnitudes of bins j + 16 k2 (and 256 on lane 0)
+    float mg[16];
+#pragma unroll
+    for (int k2 = 0; k2 < 16; ++k2) {
+      const int k = j + 16 * k2;
+      const float2 zk = x[k2], zn = T[(256 - k) & 255];
       const float2 E = make_float2(0.5f * (zk.x + zn.x), 0.5f * (zk.y - zn.y));
       const float2 O = make_float2(0.5f * (zk.y + zn.y), -0.5f * (zk.x - zn.x));
-      const float2 X = cmul(g_mel.tw[k], O);
-      const float re = E.x + X.x, im = E.y + X.y;
-      mag[w][k] = sqrtf(re * re + im * im);
+      const float2 X = cadd(E, cmul(tw512[k], O));
+      mg[k2] = sqrtf(X.x * X.x + X.y * X.y);
     }
-    if (lane == 0) mag[w][256] = fabsf(Z[0].x - Z[0].y);
-    __syncthreads();
-    // mel bands and log
+    const float m256 = fabsf(x[0].x - x[0].y);
+    wave_sync();
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      const int b = lane + 64 * r;
-      const int s = g_mel.band_start[b], cnt = g_mel.band_count[b], wo = g_mel.band_woff[b];
+    for (int k2 = 0; k2 < 16; ++k2) M[j + 16 * k2] = mg[k2];
+    if (j == 0) M[256] = m256;
+    wave_sync();
+    // mel bands j, j + 16, ..., then the log
+    float out[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int b = j + 16 * i;
+      const int s = bstart[b], cnt = bcount[b], wo = bwoff[b];
       float acc = 0.f;
-      for (int q = 0; q < cnt; ++q) acc += mag[w][s + q] * g_mel.band_w[wo + q];
-      if (active) mel[g * kMels + b] = logf(acc + kMelFloor);
+      for (int q = 0; q < cnt; ++q) acc += M[s + q] * bw[wo + q];
+      out[i] = logf(acc + kMelFloor);
     }
-    __syncthreads();
+    wave_sync();
+    // the frame's 128 outputs through LDS, then 32 contiguous bytes per lane
+    float* O = M + 260;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) O[j + 16 * i] = out[i];
+    wave_sync();
+    if (active) {
+      const float4 a = *(const float4*)(O + 8 * j), c = *(const float4*)(O + 8 * j + 4);
+      float* dst = mel + g * kMels + 8 * j;
+      *(float4*)dst = a;
+      *(float4*)(dst + 4) = c;
+    }
+    wave_sync();
   }
 }
 
@@ -200,8 +333,8 @@ hipError_t mel_tables_init() {
 hipError_t launch_logmel(const float* wave, const int64_t* sample_off, const int64_t* frame_off,
                          int B, int64_t total_frames, float* mel, hipStream_t s) {
   if (total_frames <= 0) return hipSuccess;
-  const int64_t blocks = (total_frames + 3) / 4;
-  const int grid = (int)(blocks < (1 << 20) ? blocks : (1 << 20));
+  const int64_t blocks = (total_frames + FPB - 1) / FPB;
+  const int grid = (int)(blocks < 4096 ? blocks : 4096);
   hipLaunchKernelGGL(k_logmel, dim3(grid), dim3(256), 0, s, wave, sample_off, frame_off, B,
                      total_frames, mel);
   return hipGetLastError();
