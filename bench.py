@@ -8,9 +8,14 @@ batch, inputs already resident in HBM. Prints one JSON line.
 
   python bench.py [--gpus 1] [--steps 20] [--warmup 5]
                   [--workload batch32|frontend256|ragged64]
-                  [--kernel gemm_ffn1] [--no-cpu-baseline]
+                  [--kernel gemm_ffn1] [--no-cpu-baseline] [--copy-probe]
+
+--copy-probe runs one plain 256 MiB device-to-device copy after the timed
+region; under rocprofv3 --pmc it is the calibration for FETCH_SIZE and
+WRITE_SIZE (the counters' reading for a known byte count).
 """
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -25,6 +30,15 @@ METRIC = "audio-seconds encoded/sec (log-mel + 12-layer Conformer, batch 32); % 
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_F32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
+
+# HBM traffic per launch measured with rocprofv3 counters; valid only while
+# the kernel sources hash to what they were when the counters were taken.
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "traffic_batch32.md")
+KERNEL_SOURCES = {
+    "logmel": ["logmel.hip", "common.h"],
+    "gemm": ["gemm.hip", "launch.h", "common.h"],
+}
+COPY_PROBE_BYTES = 256 << 20
 
 
 def log(msg):
@@ -41,6 +55,32 @@ def gemm_flops_per_launch(cls, tokens, cfg):
         "gemm_lcstart": 2.0 * tokens * 2 * d * d,
         "gemm_lcend": 2.0 * tokens * d * d,
     }[cls]
+
+
+def sources_sha256(kclass):
+    files = KERNEL_SOURCES["logmel" if kclass == "logmel" else "gemm"]
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "log_mel_conformer_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(kclass, workload):
+    """Bytes per launch from the committed counter record, or None when there
+    is no record for this kernel and workload or its sources have changed."""
+    try:
+        with open(TRAFFIC_RECORD) as fh:
+            text = fh.read()
+    except OSError:
+        return None
+    for block in text.split("```json")[1:]:
+        rec = json.loads(block.split("```")[0])
+        if rec.get("kernel_class") == kclass and rec.get("workload") == workload:
+            if rec.get("sources_sha256") != sources_sha256(kclass):
+                return None
+            return float(rec["hbm_bytes_per_launch"])
+    return None
 
 
 def cpu_baseline(clip, W, seconds):
@@ -64,6 +104,7 @@ def main():
     ap.add_argument("--workload", default="batch32", choices=["batch32", "frontend256", "ragged64"])
     ap.add_argument("--kernel", default="gemm_ffn1")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for {args.gpus}); "
@@ -120,6 +161,13 @@ def main():
     launches, kms = ae.timing_read()
     ae.timing_enable(None)
     ms = (t1 - t0) * 1e3 / args.steps
+    if args.copy_probe:
+        src = torch.ones(COPY_PROBE_BYTES // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     value = audio_s / (ms / 1e3)
     avg_ms = kms / max(launches, 1)
 
@@ -128,13 +176,15 @@ def main():
         per_launch = 4.0 * float(pl["sample_off"][-1]) + 4.0 * 128 * frames
         achieved = per_launch / (avg_ms / 1e3) / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": achieved / PEAK_HBM_GBS, "traffic": None, "kernel": "k_logmel",
+                "frac": achieved / PEAK_HBM_GBS,
+                "traffic": recorded_traffic(kclass, args.workload), "kernel": "k_logmel",
                 "avg_ms": avg_ms, "launches": launches}
     else:
         flops = gemm_flops_per_launch(kclass, tokens, model.cfg)
         achieved = flops / (avg_ms / 1e3) / 1e12
         roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+                "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+                "traffic": recorded_traffic(kclass, args.workload),
                 "kernel": kclass, "avg_ms": avg_ms, "launches": launches}
 
     cpu = None

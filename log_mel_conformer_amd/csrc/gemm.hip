@@ -161,6 +161,153 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, f32x16 (&acc)[MT][
   }
 }
 
+// Four values to or from LDS as one access (8 bytes of bf16, 16 of float).
+__device__ __forceinline__ void put4(unsigned char* p, const float* o) {
+  *(float4*)p = make_float4(o[0], o[1], o[2], o[3]);
+}
+__device__ __forceinline__ void put4_bf16(unsigned char* p, const float* o) {
+  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+  bf16x4 v = {(bf16)o[0], (bf16)o[1], (bf16)o[2], (bf16)o[3]};
+  *(bf16x4*)p = v;
+}
+template <typename TS> __device__ __forceinline__ void put4s(unsigned char* p, const float* o) {
+  if (std::is_same<TS, float>::value) put4(p, o);
+  else put4_bf16(p, o);
+}
+template <typename TS> __device__ __forceinline__ void get4s(const unsigned char* p, float* o) {
+  if (std::is_same<TS, float>::value) {
+    const float4 v = *(const float4*)p;
+    o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w;
+  } else {
+    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+    const bf16x4 v = *(const bf16x4*)p;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = (float)v[e];
+  }
+}
+
+constexpr int staged_slabs(int mt, int slab, int ldsb) {
+  int best = 1;
+  for (int s = 1; s <= mt; ++s)
+    if (mt % s == 0 && s * slab <= ldsb) best = s;
+  return best;
+}
+
+// Epilogue of a k_gemm_dl tile, staged through the (then idle) LDS. From
+// the accumulators a lane owns four consecutive columns of 32 different
+// rows per store, which reaches the L2 as partial-line writes from every CU
+// at once. Instead, every wavefront writes its epilogue values into a
+// row-major LDS image of SPI 32-row slabs (pitch padded by one access, so
+// the 32 rows of a write land in distinct banks), and after a barrier the
+// block stores whole rows, consecutive lanes on consecutive bytes. The
+// light conv's residual add happens in that second phase, so the residual
+// is read with the same row-contiguous pattern. Values match the direct
+// epilogue exactly (same arithmetic, same rounding points).
+template <typename TO, int BM, int BN, int WM, int WN, int EPI, int LDSB>
+__device__ __forceinline__ void epilogue_staged(const GemmParams& p,
+                                                f32x16 (&acc)[BM / WM / 32][BN / WN / 32],
+                                                unsigned char* smem, int m0, int n0, int wm,
+                                                int wn, int seg, int wave, int lane) {
+  constexpr int NW = WM * WN, WTM = BM / WM, WTN = BN / WN, MT = WTM / 32, NTL = WTN / 32;
+  constexpr bool GLU = EPI == EPI_GLU;
+  constexpr int OUTN = GLU ? BN / 2 : BN, WOUT = OUTN / WN;
+  using TS = typename std::conditional<EPI == EPI_RESID, float, TO>::type;
+  constexpr int ES = sizeof(TS), VB = 4 * ES;
+  constexpr int PITCH = OUTN * ES + VB;
+  constexpr int SLAB = WM * 32 * PITCH;
+  static_assert(SLAB <= LDSB, "one slab must fit the staging space");
+  constexpr int SPI = staged_slabs(MT, SLAB, LDSB);
+  constexpr int R = WM * SPI * 32;  // staged rows per pass
+  constexpr int LPR = OUTN / 4;     // lanes per staged row
+  static_assert(64 % LPR == 0, "whole rows per wavefront access");
+  constexpr int RPI = 64 / LPR;     // rows per wavefront access
+  static_assert((R / RPI) % NW == 0, "row groups spread evenly over wavefronts");
+  static_assert(EPI != EPI_LNRELU, "conv1's epilogue is not staged");
+
+  const int r = lane & 31, h = lane >> 5;
+  const float lo = p.olo[GLU ? 0 : seg], hi = p.ohi[GLU ? 0 : seg];
+  const int ocol0 = GLU ? n0 / 2 : n0;
+  TO* C = (TO*)p.C;
+  // every wavefront is past its last fragment read, and the main loop's
+  // final (unused) refill has landed, before the stage buffers are reused
+  __syncthreads();
+#pragma unroll
+  for (int pass = 0; pass < MT / SPI; ++pass) {
+    if (pass > 0) __syncthreads();
+#pragma unroll
+    for (int s = 0; s < SPI; ++s) {
+      const int i = pass * SPI + s;
+      unsigned char* srow = smem + (wm * SPI * 32 + s * 32 + r) * PITCH;
+      if (GLU) {
+#pragma unroll
+        for (int jp = 0; jp < NTL / 2; ++jp)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int c = wn * WOUT + jp * 32 + g * 8 + h * 4;
+            float o[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float a = clampf(acc[i][2 * jp][4 * g + e], lo, hi);
+              const float b = clampf(acc[i][2 * jp + 1][4 * g + e], lo, hi);
+              o[e] = a * sigmoidf_(b);
+            }
+            put4s<TS>(srow + c * ES, o);
+          }
+      } else {
+#pragma unroll
+        for (int j = 0; j < NTL; ++j)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int c = wn * WOUT + j * 32 + g * 8 + h * 4;
+            const int col = ocol0 + c;
+            float o[4];
+            if (EPI == EPI_STORE) {
+              float4 sc = make_float4(1.f, 1.f, 1.f, 1.f);
+              if (p.colscale) sc = *(const float4*)(p.colscale + col);
+              const float scv[4] = {sc.x, sc.y, sc.z, sc.w};
+#pragma unroll
+              for (int e = 0; e < 4; ++e) o[e] = clampf(acc[i][j][4 * g + e], lo, hi) * scv[e];
+            } else if (EPI == EPI_SILU) {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const float y = clampf(acc[i][j][4 * g + e], lo, hi);
+                o[e] = clampf(y * sigmoidf_(y), p.nlo, p.nhi);
+              }
+            } else if (EPI == EPI_RESID) {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) o[e] = clampf(acc[i][j][4 * g + e], lo, hi);
+            } else {  // EPI_BIAS
+              const float4 bv = *(const float4*)(p.bias + col);
+              o[0] = acc[i][j][4 * g] + bv.x;
+              o[1] = acc[i][j][4 * g + 1] + bv.y;
+              o[2] = acc[i][j][4 * g + 2] + bv.z;
+              o[3] = acc[i][j][4 * g + 3] + bv.w;
+            }
+            put4s<TS>(srow + c * ES, o);
+          }
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < R / RPI / NW; ++t) {
+      const int sr = (t * NW + wave) * RPI + lane / LPR;
+      const int c = (lane % LPR) * 4;
+      const int wr = sr / (SPI * 32), w = sr - wr * (SPI * 32);
+      const int grow = m0 + wr * WTM + (pass * SPI + w / 32) * 32 + (w & 31);
+      if (grow < p.M) {
+        float o[4];
+        get4s<TS>(smem + sr * PITCH + c * ES, o);
+        TO* dst = C + (size_t)grow * p.ldc + ocol0 + c;
+        if (EPI == EPI_RESID) {
+          const float4 hv = *(const float4*)dst;
+          o[0] += hv.x; o[1] += hv.y; o[2] += hv.z; o[3] += hv.w;
+        }
+        store4(dst, o[0], o[1], o[2], o[3]);
+      }
+    }
+  }
+}
+
 template <typename T, typename TO, int BM, int BN, int WM, int WN, int AL, int EPI>
 __global__ void __launch_bounds__(WM * WN * 64) k_gemm(GemmParams p) {
   constexpr int NTH = WM * WN * 64;
@@ -542,7 +689,14 @@ __global__ void __launch_bounds__(WM * WN * 64, OCC) k_gemm_dl(GemmParams p) {
       mfmas(cur, st + 1 < NSUB ? NLOAD : 0, 0);
     }
   }
-  epilogue<TO, MT, NTL, EPI>(p, acc, m0 + wm * WTM, n0 + wn * WTN, seg, lane);
+  // Staging wins where the epilogue is light (plain store, residual add,
+  // bias); SiLU and GLU spend enough arithmetic per value that storing
+  // straight from registers, overlapped with that arithmetic, is faster.
+  if constexpr (EPI == EPI_SILU || EPI == EPI_GLU)
+    epilogue<TO, MT, NTL, EPI>(p, acc, m0 + wm * WTM, n0 + wn * WTN, seg, lane);
+  else
+    epilogue_staged<TO, BM, BN, WM, WN, EPI, STAGES * STAGE>(p, acc, smem, m0, n0, wm, wn, seg,
+                                                            wave, lane);
 }
 
 template <typename T, typename TO, int BM, int BN, int WM, int WN, int RB, int STAGES, int EPI,
@@ -584,11 +738,14 @@ hipError_t dispatch_f32(int epi, int aload, const GemmParams& p, hipStream_t s) 
 //  narrow (otherwise):               256x128, 8 wavefronts of 64x64, two blocks per CU
 template <int EPI, typename TO>
 hipError_t run_bf16(const GemmParams& p, hipStream_t s) {
+  // measured inside the encoder (24000 rows): 256x256 tiles in bands of 4
+  // row tiles for the wide projections, 192x256 with two blocks per CU for
+  // the deep one, two 256x128 blocks per CU for the square ones
   if (p.N % 256 == 0 && p.N >= 2048)
-    return run_dl<bf16, TO, 256, 256, 2, 4, 128, 2, EPI>(p, s);
+    return run_dl<bf16, TO, 256, 256, 2, 4, 128, 2, EPI, 1, 4>(p, s);
   if (p.K >= 2048 && p.N % 256 == 0)
-    return run_dl<bf16, TO, 192, 256, 2, 2, 64, 3, EPI, 2>(p, s);
-  return run_dl<bf16, TO, 256, 128, 4, 2, 64, 3, EPI, 2>(p, s);
+    return run_dl<bf16, TO, 192, 256, 2, 2, 64, 3, EPI, 2, 4>(p, s);
+  return run_dl<bf16, TO, 256, 128, 4, 2, 64, 3, EPI, 2, 2>(p, s);
 }
 
 hipError_t dispatch_bf16(int epi, int aload, bool out_bf16, const GemmParams& p, hipStream_t s) {
