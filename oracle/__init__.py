@@ -11,7 +11,9 @@ Source of the method: the docs.rs source page of cortiq-engine 0.8.49,
 ``cortiq_engine/egemma2_audio.rs`` (the ``gemma4_audio`` tower of
 EmbeddingGemma 2), cited below as "egemma2_audio.rs" with the item it
 defines; the RMS-norm form comes from the cortiq-engine 0.5.94
-``ltxdit.rs`` page (``rms_plain`` / ``rms_w``).
+``ltxdit.rs`` page (``rms_plain`` / ``rms_w``). The same egemma2_audio.rs
+page defines the step ahead of the log-mel, mixdown and resampling to
+16 kHz (``oracle.resample``).
 
 Every function is pinned by a CPU test (values the pages print, closed
 forms, invariants, library cross-checks or brute force); the one result with
@@ -26,3 +28,5 @@ from .tower import (layer_norm_relu, subsample, rms_norm, clip_linear, silu,
                     local_attention, attention_block, glu, causal_dwconv,
                     light_conv, conformer_layer, head, encode_clips,
                     tower_constants)
+from .resample import (bessel_i0, resampled_length, cutoff, kernel as resample_kernel,
+                       resample, resample_f64, mixdown, to_mono_16k)
