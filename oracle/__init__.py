@@ -28,5 +28,4 @@ from .tower import (layer_norm_relu, subsample, rms_norm, clip_linear, silu,
                     local_attention, attention_block, glu, causal_dwconv,
                     light_conv, conformer_layer, head, encode_clips,
                     tower_constants)
-from .resample import (bessel_i0, resampled_length, cutoff, kernel as resample_kernel,
-                       resample, resample_f64, mixdown, to_mono_16k)
+from . import resample  # the module: oracle.resample.resample, .mixdown, ...
