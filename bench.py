@@ -7,7 +7,7 @@ residual stream; random-init weights. A step is one ae_encode over the
 batch, inputs already resident in HBM. Prints one JSON line.
 
   python bench.py [--gpus 1] [--steps 20] [--warmup 5]
-                  [--workload batch32|frontend256|ragged64]
+                  [--workload batch32|frontend256|ragged64|resample48k]
                   [--kernel gemm_ffn1] [--no-cpu-baseline] [--copy-probe]
 
 --copy-probe runs one plain 256 MiB device-to-device copy after the timed
@@ -30,6 +30,7 @@ METRIC = "audio-seconds encoded/sec (log-mel + 12-layer Conformer, batch 32); % 
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_F32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
+PEAK_F64_TFLOPS = 78.6   # fp64 vector FMA: 256 CUs x 64 lanes x 2 flops x 2.4 GHz
 
 # HBM traffic per launch measured with rocprofv3 counters; valid only while
 # the kernel sources hash to what they were when the counters were taken.
@@ -37,6 +38,7 @@ TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "traffic_batch32.md")
 KERNEL_SOURCES = {
     "logmel": ["logmel.hip", "common.h"],
     "gemm": ["gemm.hip", "launch.h", "common.h"],
+    "resample": ["resample.hip", "launch.h", "common.h"],
 }
 COPY_PROBE_BYTES = 256 << 20
 
@@ -58,7 +60,7 @@ def gemm_flops_per_launch(cls, tokens, cfg):
 
 
 def sources_sha256(kclass):
-    files = KERNEL_SOURCES["logmel" if kclass == "logmel" else "gemm"]
+    files = KERNEL_SOURCES[kclass if kclass in KERNEL_SOURCES else "gemm"]
     h = hashlib.sha256()
     for f in files:
         with open(os.path.join(ROOT, "log_mel_conformer_amd", "csrc", f), "rb") as fh:
@@ -96,12 +98,72 @@ def cpu_baseline(clip, W, seconds):
                       f"encoder in float64 numpy, {dt:.1f} s wall"}
 
 
+def bench_resample(args, torch, ae, synth):
+    """32 clips x 30 s of stereo at 48 kHz -> mono 16 kHz (mixdown and the
+    Kaiser-sinc resampler, float64 accumulation)."""
+    clips = synth.recorded_batch(32, 48000, 30.0)
+    data_np, off = synth.pack_frames(clips)
+    data = torch.from_numpy(data_np).cuda()
+    r = ae.Resampler(48000, 16000)
+    oo = r.out_offsets(off)
+    y = torch.empty(int(oo[-1]), dtype=torch.float32, device="cuda")
+    step = lambda: ae.to_mono_16k(r, data, off, 2, out=y)  # noqa: E731
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ae.timing_enable("resample")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    launches, kms = ae.timing_read()
+    ae.timing_enable(None)
+    ms = (t1 - t0) * 1e3 / args.steps
+    audio_s = float(off[-1]) / 48000.0
+    info = r.info()
+    # the method's multiply-adds: the taps inside the window of every output
+    macs = info["nonzero_taps_per_cycle"] / info["phases"] * float(oo[-1])
+    avg_ms = kms / max(launches, 1)
+    achieved = 2.0 * macs / (avg_ms / 1e3) / 1e12
+    roof = {"bound": "alu", "achieved": achieved, "peak": PEAK_F64_TFLOPS, "unit": "TFLOP/s",
+            "frac": achieved / PEAK_F64_TFLOPS,
+            "traffic": recorded_traffic("resample", args.workload), "kernel": "k_resample",
+            "avg_ms": avg_ms, "launches": launches}
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle.resample as ors
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        c0 = clips[0]
+        t0 = time.perf_counter()
+        ors.to_mono_16k([c0[:, 0], c0[:, 1]], 48000)
+        dt = time.perf_counter() - t0
+        cpu = {"value": 30.0 / dt, "unit": "audio-s/s", "cores": threads, "kind": "oracle",
+               "sample": f"1 clip of the workload (30 s stereo at 48 kHz) through the oracle's "
+                         f"mixdown and resampler, float64 numpy, {dt:.1f} s wall"}
+    r.close()
+    rec = {"metric": "audio-seconds resampled/sec (stereo 48 kHz -> mono 16 kHz, batch 32)",
+           "value": audio_s / (ms / 1e3), "unit": "audio-s/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "f64",
+           "data": "synthetic (seeded multisine + noise, two channels)",
+           "config": {"workload": "32 clips x 30 s stereo 48 kHz: mixdown + Kaiser-sinc "
+                                  "resampling to 16 kHz (float64 accumulation)",
+                      "global_batch": 32, "audio_seconds": audio_s,
+                      "output_samples": int(oo[-1]), "parallelism": "none (1 GPU)"},
+           "roofline": roof, "cpu_baseline": cpu}
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="batch32", choices=["batch32", "frontend256", "ragged64"])
+    ap.add_argument("--workload", default="batch32",
+                    choices=["batch32", "frontend256", "ragged64", "resample48k"])
     ap.add_argument("--kernel", default="gemm_ffn1")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true")
@@ -117,6 +179,8 @@ def main():
 
     torch.cuda.set_device(0)
     log(f"[bench] workload {args.workload}: generating inputs")
+    if args.workload == "resample48k":
+        return bench_resample(args, torch, ae, synth)
     if args.workload == "batch32":
         clips = synth.multisine_batch(32)
     elif args.workload == "ragged64":

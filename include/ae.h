@@ -188,6 +188,68 @@ ae_status ae_encode(const ae_model* m, const float* wave, const int64_t* sample_
                     int32_t B, float* out, float* const* trace, void* ws, size_t ws_bytes,
                     ae_stream stream);
 
+/* --- mixdown and resampling to 16 kHz (ahead of ae_logmel) -------------
+ * The page: to_mono_16k, resample_hq and the resampler constants. */
+
+/* Samples after resampling n samples from from_rate to to_rate (Hz): n for
+ * equal rates, else ceil(to_rate * n / from_rate). -1 for n < 0, a
+ * non-positive rate, or a result beyond int64. */
+int64_t ae_resampled_length(int64_t n, int32_t from_rate, int32_t to_rate);
+
+typedef struct ae_resampler ae_resampler; /* opaque */
+
+/* Plans band-limited resampling from from_rate to to_rate (each 1..768000
+ * Hz) on the current device: with g = gcd, o = from/g, nw = to/g and
+ * c = min(1, to/from) * 0.958, output m is
+ *   sum over the clip's samples n of x[n] h(n - m from/to),
+ *   h(d) = c sinc(c d) I0(12.8 sqrt(1 - (c d / 64)^2)) / I0(12.8), |c d| < 64,
+ * (a Kaiser-windowed sinc with 64 zero crossings a side, beta 12.8, cut-off
+ * at 0.958 of the lower Nyquist rate), accumulated in float64, rounded to
+ * float32. Allocates and fills a device table of the nw phases' taps
+ * (float64) with work on `stream`, and waits for it. Equal rates plan a
+ * copy. AE_ERR_INVALID for rates out of range, AE_ERR_UNSUPPORTED when the
+ * kernel's working set does not fit a CU's LDS or the table would exceed
+ * 2^28 entries, AE_ERR_HIP when an allocation fails. */
+ae_status ae_resampler_create(int32_t from_rate, int32_t to_rate, ae_stream stream,
+                              ae_resampler** out);
+/* Frees the table; no work using the resampler may still be queued. */
+void ae_resampler_destroy(ae_resampler* r);
+/* Plan facts for measurement (each output nullable): the largest tap count
+ * of a phase, the nonzero taps summed over the nw phases (the method's
+ * multiply-adds per nw outputs), nw and o. */
+ae_status ae_resampler_info(const ae_resampler* r, int32_t* taps_per_phase_max,
+                            int64_t* nonzero_taps_per_cycle, int32_t* phases,
+                            int32_t* in_per_cycle);
+/* Workspace bytes for ae_resample (channels = 1) or ae_to_mono_16k with B
+ * clips of total_frames input frames. */
+size_t ae_resample_workspace_bytes(int32_t B, int64_t total_frames, int32_t channels);
+
+/* Channel mixdown (the page: to_mono_16k): in: device float
+ * [n_frames][channels], interleaved; mono: device float [n_frames]; each
+ * output is the channel values added in float32 in channel order, divided
+ * by `channels` in float32 (one channel is copied). channels >= 1. */
+ae_status ae_mixdown(const float* in, int64_t n_frames, int32_t channels, float* mono,
+                     ae_stream stream);
+
+/* Resampling of B packed clips (the page: resample_hq): x: device float,
+ * clip i at [in_off[i], in_off[i+1]) (host int64 [B+1], in_off[0] = 0,
+ * non-decreasing); y: device float, clip after clip, clip i holding
+ * ae_resampled_length(length i, from, to) samples. Samples outside a clip
+ * are absent from its sums. ws: device workspace of at least
+ * ae_resample_workspace_bytes(B, in_off[B], 1) bytes (unused for equal
+ * rates); it must be on the resampler's device. */
+ae_status ae_resample(const ae_resampler* r, const float* x, const int64_t* in_off, int32_t B,
+                      float* y, void* ws, size_t ws_bytes, ae_stream stream);
+
+/* Mixdown then resampling to 16 kHz (the page: to_mono_16k): in: device
+ * float, B clips of interleaved frames [frames][channels], clip i at frames
+ * [in_off[i], in_off[i+1]); y as ae_resample's output. The resampler must
+ * target 16000 Hz. ws: ae_resample_workspace_bytes(B, in_off[B], channels)
+ * bytes (the mono signal lives there). */
+ae_status ae_to_mono_16k(const ae_resampler* r, const float* in, const int64_t* in_off,
+                         int32_t B, int32_t channels, float* y, void* ws, size_t ws_bytes,
+                         ae_stream stream);
+
 /* --- measurement ----------------------------------------------------- */
 
 /* Kernel classes the library can time with HIP events recorded on the
@@ -198,7 +260,7 @@ typedef enum {
   AE_K_LOGMEL = 0, AE_K_CONV0 = 1, AE_K_CONV1 = 2, AE_K_GEMM_FFN1 = 3,
   AE_K_GEMM_FFN2 = 4, AE_K_GEMM_QKV = 5, AE_K_GEMM_POST = 6, AE_K_GEMM_LCSTART = 7,
   AE_K_GEMM_LCEND = 8, AE_K_GEMM_HEAD = 9, AE_K_ROWNORM = 10, AE_K_ATTN = 11,
-  AE_K_LCONV = 12, AE_K_COUNT = 13
+  AE_K_LCONV = 12, AE_K_RESAMPLE = 13, AE_K_MIXDOWN = 14, AE_K_COUNT = 15
 } ae_kernel_class;
 
 /* Process-wide: from now on, bracket every launch of kernel class `cls`

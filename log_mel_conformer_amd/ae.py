@@ -7,7 +7,9 @@ There is no fallback: if libae.so is missing, importing the library
 raises.
 
 Names follow include/ae.h: ``logmel``, ``subsample``, ``conformer_layer``,
-``encode``, ``num_frames``, ``num_tokens``, ``plan``, ``Model``.
+``encode``, ``num_frames``, ``num_tokens``, ``plan``, ``Model``, and for the
+step ahead of the log-mel ``resampled_length``, ``Resampler``, ``mixdown``,
+``resample``, ``to_mono_16k``.
 """
 from __future__ import annotations
 
@@ -21,7 +23,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libae.so")
 AE_OK, AE_ERR_INVALID, AE_ERR_SHAPE, AE_ERR_CAPACITY, AE_ERR_UNSUPPORTED, AE_ERR_HIP = range(6)
 AE_F32, AE_BF16 = 0, 1
 KERNEL_CLASSES = ("logmel", "conv0", "conv1", "gemm_ffn1", "gemm_ffn2", "gemm_qkv", "gemm_post",
-                  "gemm_lcstart", "gemm_lcend", "gemm_head", "rownorm", "attn", "lconv")
+                  "gemm_lcstart", "gemm_lcend", "gemm_head", "rownorm", "attn", "lconv",
+                  "resample", "mixdown")
 
 
 class AeError(RuntimeError):
@@ -89,6 +92,16 @@ def lib():
             "ae_subsample": (C.c_int, [_P, _P, i64p, C.c_int32, _P, _P, C.c_size_t, _P]),
             "ae_conformer_layer": (C.c_int, [_P, C.c_int32, _P, _P, C.c_int64, _P, C.c_size_t, _P]),
             "ae_encode": (C.c_int, [_P, _P, i64p, C.c_int32, _P, C.POINTER(_P), _P, C.c_size_t, _P]),
+            "ae_resampled_length": (C.c_int64, [C.c_int64, C.c_int32, C.c_int32]),
+            "ae_resampler_create": (C.c_int, [C.c_int32, C.c_int32, _P, C.POINTER(_P)]),
+            "ae_resampler_destroy": (None, [_P]),
+            "ae_resampler_info": (C.c_int, [_P, C.POINTER(C.c_int32), i64p,
+                                            C.POINTER(C.c_int32), C.POINTER(C.c_int32)]),
+            "ae_resample_workspace_bytes": (C.c_size_t, [C.c_int32, C.c_int64, C.c_int32]),
+            "ae_mixdown": (C.c_int, [_P, C.c_int64, C.c_int32, _P, _P]),
+            "ae_resample": (C.c_int, [_P, _P, i64p, C.c_int32, _P, _P, C.c_size_t, _P]),
+            "ae_to_mono_16k": (C.c_int, [_P, _P, i64p, C.c_int32, C.c_int32, _P, _P, C.c_size_t,
+                                         _P]),
             "ae_timing_enable": (C.c_int, [C.c_int32]),
             "ae_timing_read": (C.c_int, [i64p, C.POINTER(C.c_double)]),
         }
@@ -303,6 +316,99 @@ def encode(model: Model, wave, sample_off, out=None, trace: bool = False):
                            C.cast(tr_arr, C.POINTER(C.c_void_p)) if tr_arr is not None else None,
                            _ptr(ws), ws.numel(), _stream()))
     return (out, tr) if trace else out
+
+
+def resampled_length(n: int, from_rate: int, to_rate: int = 16000) -> int:
+    v = int(lib().ae_resampled_length(int(n), int(from_rate), int(to_rate)))
+    if v < 0:
+        raise AeError(AE_ERR_INVALID, f"no resampled length for n={n}, {from_rate} -> {to_rate}")
+    return v
+
+
+class Resampler:
+    """A planned rate conversion (ae_resampler_create): the per-phase tap
+    table lives on the current device until close()."""
+
+    def __init__(self, from_rate: int, to_rate: int = 16000):
+        self.from_rate, self.to_rate = int(from_rate), int(to_rate)
+        h = C.c_void_p()
+        _check(lib().ae_resampler_create(self.from_rate, self.to_rate, _stream(), C.byref(h)))
+        self.handle = h
+        self._ws = None
+
+    def info(self) -> dict:
+        q, ph, o = C.c_int32(), C.c_int32(), C.c_int32()
+        nz = C.c_int64()
+        _check(lib().ae_resampler_info(self.handle, C.byref(q), C.byref(nz), C.byref(ph),
+                                       C.byref(o)))
+        return {"taps_per_phase_max": q.value, "nonzero_taps_per_cycle": nz.value,
+                "phases": ph.value, "in_per_cycle": o.value}
+
+    def out_offsets(self, in_off) -> np.ndarray:
+        lens = np.diff(np.asarray(in_off, dtype=np.int64))
+        out = np.zeros(len(lens) + 1, dtype=np.int64)
+        out[1:] = np.cumsum([resampled_length(n, self.from_rate, self.to_rate) for n in lens])
+        return out
+
+    def workspace(self, B: int, frames: int, channels: int, device):
+        import torch
+        need = max(int(lib().ae_resample_workspace_bytes(B, frames, channels)), 256)
+        if self._ws is None or self._ws.numel() < need or self._ws.device != device:
+            self._ws = torch.empty(need, dtype=torch.uint8, device=device)
+        return self._ws
+
+    def close(self):
+        if getattr(self, "handle", None) is not None and _lib is not None:
+            import torch
+            torch.cuda.synchronize()
+            lib().ae_resampler_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def mixdown(x, channels: int, out=None):
+    """x: cuda float32 [frames, channels] (or flat, interleaved) -> [frames]."""
+    import torch
+    frames = x.numel() // channels
+    if out is None:
+        out = torch.empty(frames, dtype=torch.float32, device=x.device)
+    _check(lib().ae_mixdown(_ptr(x), frames, channels, _ptr(out), _stream()))
+    return out
+
+
+def resample(r: Resampler, x, in_off, out=None):
+    """x: cuda float32 [sum N], clip i at [in_off[i], in_off[i+1]) -> the
+    clips resampled, packed."""
+    import torch
+    io, ip = _i64(in_off)
+    B = len(io) - 1
+    total = int(r.out_offsets(io)[-1])
+    if out is None:
+        out = torch.empty(total, dtype=torch.float32, device=x.device)
+    ws = r.workspace(B, int(io[-1]), 1, x.device)
+    _check(lib().ae_resample(r.handle, _ptr(x), ip, B, _ptr(out), _ptr(ws), ws.numel(),
+                             _stream()))
+    return out
+
+
+def to_mono_16k(r: Resampler, x, in_off, channels: int, out=None):
+    """x: cuda float32 [sum N, channels] interleaved frames, clip i at frames
+    [in_off[i], in_off[i+1]) -> mono 16 kHz clips, packed."""
+    import torch
+    io, ip = _i64(in_off)
+    B = len(io) - 1
+    total = int(r.out_offsets(io)[-1])
+    if out is None:
+        out = torch.empty(total, dtype=torch.float32, device=x.device)
+    ws = r.workspace(B, int(io[-1]), channels, x.device)
+    _check(lib().ae_to_mono_16k(r.handle, _ptr(x), ip, B, channels, _ptr(out), _ptr(ws),
+                                ws.numel(), _stream()))
+    return out
 
 
 def timing_enable(cls):

@@ -60,6 +60,41 @@ def multisine_clip(seed: int = 0, n: int = MAX_SAMPLES) -> np.ndarray:
     return x.astype(np.float32)
 
 
+def recorded_clip(seed: int, rate: int, seconds: float, channels: int = 2) -> np.ndarray:
+    """A clip as a recorder delivers it, ahead of mixdown and resampling:
+    interleaved frames [n, channels] float32 at `rate`, n = rate * seconds.
+    Every channel holds the same 8 sines (frequencies U(50, 0.45 rate) Hz,
+    amplitudes U(0, 0.1), drawn in that order, zero phase) plus its own
+    N(0, 0.02^2) noise, so content sits above the 8 kHz a 16 kHz signal can
+    keep as well as below it."""
+    rng = np.random.default_rng(seed)
+    n = int(round(rate * seconds))
+    f = rng.uniform(50.0, 0.45 * rate, 8)
+    a = rng.uniform(0.0, 0.1, 8)
+    t = np.arange(n, dtype=np.float64) / rate
+    base = np.zeros(n, dtype=np.float64)
+    for fk, ak in zip(f, a):
+        base += ak * np.sin(2 * np.pi * fk * t)
+    out = np.empty((n, channels), dtype=np.float32)
+    for c in range(channels):
+        out[:, c] = (base + rng.normal(0.0, 0.02, n)).astype(np.float32)
+    return out
+
+
+def recorded_batch(clips: int, rate: int, seconds: float, channels: int = 2):
+    return [recorded_clip(i, rate, seconds, channels) for i in range(clips)]
+
+
+def pack_frames(clips):
+    """Interleaved multichannel clips back to back: ([sum n, channels]
+    float32, frame offsets int64 [B+1])."""
+    off = np.zeros(len(clips) + 1, dtype=np.int64)
+    off[1:] = np.cumsum([len(c) for c in clips])
+    ch = clips[0].shape[1] if clips else 1
+    data = (np.concatenate(clips, axis=0) if clips else np.zeros((0, ch), np.float32))
+    return np.ascontiguousarray(data, dtype=np.float32), off
+
+
 def white_clip(seed: int = 0, n: int = MAX_SAMPLES) -> np.ndarray:
     return np.random.default_rng(seed).uniform(-1.0, 1.0, n).astype(np.float32)
 

@@ -107,3 +107,24 @@ def test_logmel_refuses_small_workspace_before_device_work():
 def test_timing_class_validation():
     assert ae.lib().ae_timing_enable(99) == ae.AE_ERR_INVALID
     assert ae.lib().ae_timing_enable(-1) == ae.AE_OK
+
+
+def test_resampled_length_matches_oracle():
+    from oracle import resample as ors
+    L = ae.lib()
+    for fr in (8000, 11025, 16000, 22050, 44100, 44099, 48000, 96000, 384000, 7):
+        for n in (0, 1, 2, 3, 160, 44099, 48000, 1440000, 123457):
+            assert L.ae_resampled_length(n, fr, 16000) == ors.resampled_length(n, fr, 16000)
+    assert L.ae_resampled_length(-1, 48000, 16000) == -1
+    assert L.ae_resampled_length(10, 0, 16000) == -1
+
+
+def test_resampler_create_refuses_bad_rates_before_any_device_work():
+    import ctypes as C
+    L = ae.lib()
+    h = C.c_void_p()
+    for fr, to in ((0, 16000), (48000, -1), (768001, 16000)):
+        assert L.ae_resampler_create(fr, to, None, C.byref(h)) == ae.AE_ERR_INVALID
+        assert h.value is None
+    assert L.ae_resample_workspace_bytes(4, 1000, 1) == 256
+    assert L.ae_resample_workspace_bytes(4, 1000, 2) == 256 + 4096
