@@ -140,6 +140,87 @@ __global__ void __launch_bounds__(kWaves * 64) k_resample(const float* __restric
   }
 }
 
+// Phase-major copy of the taps with zero padding for the blocked kernel:
+// hp[j * qp + padl + q] = table[q][j] for q < qmax, zero elsewhere.
+__global__ void k_resample_pad(const double* __restrict__ table, int nw, int qmax, int padl,
+                               int qp, double* __restrict__ hp) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (int64_t)nw * qp) return;
+  const int j = (int)(i / qp), k = (int)(i - (int64_t)j * qp) - padl;
+  hp[i] = (k >= 0 && k < qmax) ? table[(int64_t)k * nw + j] : 0.0;
+}
+
+struct FirGeom {
+  int o, nw, qp, padl, s8;  // s8: samples a lane walks, a multiple of 8
+  int u;                    // LDS floats per wavefront
+  const double* hp;         // [nw][qp]
+};
+
+// Blocked form for rate pairs whose tap windows overlap from frame to frame
+// (o well below the tap count): a wavefront serves ONE phase j, so its taps
+// are the same in every lane and come through scalar loads; lane l takes the
+// R consecutive frames F0 + l R + r. Frame r's taps start o r samples after
+// frame 0's, so walking the lane's samples s = 0 .. (R - 1) o + qmax once,
+// each sample read (and converted) once feeds R FMAs:
+//   acc[r] += h_j[s - o r] x[base + s]   (h_j zero outside its taps).
+template <int R>
+__global__ void __launch_bounds__(kWaves * 64) k_resample_fir(const float* __restrict__ x,
+                                                              const int64_t* __restrict__ offs,
+                                                              int B, FirGeom g,
+                                                              const int* __restrict__ lo,
+                                                              float* __restrict__ y) {
+  const int64_t* in_off = offs;
+  const int64_t* out_off = offs + (B + 1);
+  const int64_t* unit_off = offs + 2 * (B + 1);
+  extern __shared__ float xs[];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int64_t u = (int64_t)blockIdx.x * kWaves + wave;
+  const bool active = u < unit_off[B];
+  float* xw = xs + (size_t)wave * g.u;
+  int c = 0, j = 0;
+  int64_t f0 = 0, m_clip = 0;
+  if (active) {
+    c = find_clip(unit_off, B, u);
+    const int64_t ul = u - unit_off[c];
+    j = (int)(ul % g.nw);
+    f0 = (ul / g.nw) * (int64_t)(64 * R);
+    const int64_t n = in_off[c + 1] - in_off[c];
+    m_clip = out_off[c + 1] - out_off[c];
+    const int64_t p0 = f0 * g.o + lo[j];
+    const int len = 63 * R * g.o + g.s8;
+    const float* xc = x + in_off[c];
+    for (int i = lane; i < len; i += 64) {
+      const int64_t p = p0 + i;
+      xw[i] = (p >= 0 && p < n) ? xc[p] : 0.0f;
+    }
+  }
+  __syncthreads();
+  if (!active) return;
+  j = __builtin_amdgcn_readfirstlane(j);
+  const float* xl = xw + lane * R * g.o;
+  const double* hj = g.hp + (int64_t)j * g.qp + g.padl;
+  double acc[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) acc[r] = 0.0;
+  for (int s0 = 0; s0 < g.s8; s0 += 8) {
+    double xv[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) xv[k] = (double)xl[s0 + k];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const double* h = hj + s0 - r * g.o;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) acc[r] = fma(h[k], xv[k], acc[r]);
+    }
+  }
+  float* yc = y + out_off[c];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int64_t m = (f0 + (int64_t)lane * R + r) * g.nw + j;
+    if (m < m_clip) yc[m] = (float)acc[r];
+  }
+}
+
 // mono[i] = (in[i][0] + in[i][1] + ...) / channels, float32, in channel order.
 __global__ void k_mixdown(const float* __restrict__ in, int64_t n, int ch, float* __restrict__ mono) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -181,6 +262,10 @@ struct ae_resampler {
   double* table = nullptr;             // device [qmax][nw]
   int* lo = nullptr;                   // device [nw]
   std::vector<int> lo_host;
+  // blocked form (k_resample_fir), when consecutive frames' windows overlap
+  bool fir = false;
+  int fir_r = 1, qp = 0, padl = 0, s8 = 0, fir_u = 0;
+  double* hp = nullptr;                // device [nw][qp]
 };
 
 extern "C" {
@@ -250,6 +335,23 @@ ae_status ae_resampler_create(int32_t from_rate, int32_t to_rate, ae_stream stre
     }
     r->R = R;
     r->u = (int)lds_floats(R);
+    // blocked form: one phase per wavefront, R consecutive frames per lane;
+    // odd R keeps the lanes' LDS strides off the 64-bank period for odd o
+    if (2 * r->o <= r->qmax) {
+      for (int fr : {9, 5, 3, 1}) {
+        const int s8 = (((fr - 1) * r->o + r->qmax) + 7) / 8 * 8;
+        const int64_t u = (int64_t)63 * fr * r->o + s8;
+        if ((size_t)u * 4 * kWaves <= kLdsBudget || (fr == 1 && (size_t)u * 4 * kWaves <= kLdsMax)) {
+          r->fir = true;
+          r->fir_r = fr;
+          r->s8 = s8;
+          r->padl = (fr - 1) * r->o;
+          r->qp = r->padl + s8;
+          r->fir_u = (int)u;
+          break;
+        }
+      }
+    }
     const int64_t entries = (int64_t)r->qmax * r->nw;
     if (entries > ((int64_t)1 << 28)) {
       delete r;
@@ -265,11 +367,21 @@ ae_status ae_resampler_create(int32_t from_rate, int32_t to_rate, ae_stream stre
                          stream, r->o, r->nw, r->qmax, r->c, r->lo, r->table);
       e = hipGetLastError();
     }
+    if (e == hipSuccess && r->fir) {
+      const int64_t pe = (int64_t)r->nw * r->qp;
+      e = hipMalloc(&r->hp, sizeof(double) * (size_t)pe);
+      if (e == hipSuccess) {
+        hipLaunchKernelGGL(k_resample_pad, dim3((unsigned)((pe + 255) / 256)), dim3(256), 0,
+                           stream, r->table, r->nw, r->qmax, r->padl, r->qp, r->hp);
+        e = hipGetLastError();
+      }
+    }
     // the host copy of lo must outlive the asynchronous upload
     if (e == hipSuccess) e = hipStreamSynchronize(stream);
     if (e != hipSuccess) {
       if (r->table) hipFree(r->table);
       if (r->lo) hipFree(r->lo);
+      if (r->hp) hipFree(r->hp);
       delete r;
       return set_error(AE_ERR_HIP, std::string("ae_resampler_create: ") + hipGetErrorString(e));
     }
@@ -285,6 +397,7 @@ void ae_resampler_destroy(ae_resampler* r) {
   hipSetDevice(r->device);
   if (r->table) hipFree(r->table);
   if (r->lo) hipFree(r->lo);
+  if (r->hp) hipFree(r->hp);
   hipSetDevice(prev);
   delete r;
 }
@@ -350,7 +463,10 @@ ae_status ae_resample(const ae_resampler* r, const float* x, const int64_t* in_o
     int64_t units = 0;
     if (r->from != r->to) {
       const int64_t frames = (m + r->nw - 1) / r->nw;
-      units = (int64_t)r->jg * ((frames + (int64_t)r->fw * r->R - 1) / ((int64_t)r->fw * r->R));
+      if (r->fir)
+        units = (int64_t)r->nw * ((frames + 64 * r->fir_r - 1) / (64 * r->fir_r));
+      else
+        units = (int64_t)r->jg * ((frames + (int64_t)r->fw * r->R - 1) / ((int64_t)r->fw * r->R));
     }
     unit_off[i + 1] = unit_off[i] + units;
   }
@@ -375,6 +491,34 @@ ae_status ae_resample(const ae_resampler* r, const float* x, const int64_t* in_o
     return set_error(AE_ERR_CAPACITY, "ae_resample: batch too large for one launch");
   int64_t* d_offs = (int64_t*)ws;
   AE_HIP_TRY(launch_write_i64(d_offs, offs.data(), (int)offs.size(), stream));
+  const dim3 grid((unsigned)((units + kWaves - 1) / kWaves)), block(kWaves * 64);
+  if (r->fir) {
+    FirGeom fg;
+    fg.o = r->o;
+    fg.nw = r->nw;
+    fg.qp = r->qp;
+    fg.padl = r->padl;
+    fg.s8 = r->s8;
+    fg.u = r->fir_u;
+    fg.hp = r->hp;
+    const size_t lds = sizeof(float) * (size_t)r->fir_u * kWaves;
+    const void* fn = r->fir_r == 9 ? (const void*)k_resample_fir<9>
+                     : r->fir_r == 5 ? (const void*)k_resample_fir<5>
+                     : r->fir_r == 3 ? (const void*)k_resample_fir<3>
+                                     : (const void*)k_resample_fir<1>;
+    if (lds > 64 * 1024)
+      AE_HIP_TRY(hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
+    timing_begin(AE_K_RESAMPLE, stream);
+    switch (r->fir_r) {
+      case 9: hipLaunchKernelGGL(k_resample_fir<9>, grid, block, lds, stream, x, d_offs, B, fg, r->lo, y); break;
+      case 5: hipLaunchKernelGGL(k_resample_fir<5>, grid, block, lds, stream, x, d_offs, B, fg, r->lo, y); break;
+      case 3: hipLaunchKernelGGL(k_resample_fir<3>, grid, block, lds, stream, x, d_offs, B, fg, r->lo, y); break;
+      default: hipLaunchKernelGGL(k_resample_fir<1>, grid, block, lds, stream, x, d_offs, B, fg, r->lo, y); break;
+    }
+    timing_end(AE_K_RESAMPLE, stream);
+    AE_HIP_TRY(hipGetLastError());
+    return AE_OK;
+  }
   RsGeom g;
   g.o = r->o;
   g.nw = r->nw;
@@ -385,7 +529,6 @@ ae_status ae_resample(const ae_resampler* r, const float* x, const int64_t* in_o
   g.u = r->u;
   g.table = r->table;
   g.lo = r->lo;
-  const dim3 grid((unsigned)((units + kWaves - 1) / kWaves)), block(kWaves * 64);
   const size_t lds = sizeof(float) * (size_t)r->u * kWaves;
   if (lds > 64 * 1024) {
     const void* fn = r->R == 8 ? (const void*)k_resample<8>
