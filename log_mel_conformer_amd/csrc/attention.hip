@@ -7,8 +7,9 @@
 //
 // One block per (64 consecutive tokens, head). The K and V rows those
 // tokens can reach (64 + left - 1 of them) are staged in LDS in the storage
-// type (16-byte loads, rows padded to spread banks), R[0..left) of the head
-// as float. Four lanes serve one token, 32 of the 128 dimensions each: a
+// type (16-byte loads, all issued before the stores; rows padded to spread
+// banks), R[0..left) of the head as float with each 32-dimension part
+// padded to a 36-float pitch. Four lanes serve one token, 32 of the 128 dimensions each: a
 // lane forms its partial logits for every distance, two cross-lane steps
 // give all four lanes the full logits, each lane runs the (identical)
 // softmax, then accumulates its 32 output dimensions. Rows before the
@@ -54,22 +55,32 @@ __device__ __forceinline__ void store8(float* p, const float* v) {
   *(float4*)p = make_float4(v[0], v[1], v[2], v[3]);
   *(float4*)(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
 }
-// copy 8 elements of storage type (16 or 32 bytes)
-__device__ __forceinline__ void copy8(bf16* d, const bf16* s) { *(bf16x8*)d = *(const bf16x8*)s; }
-__device__ __forceinline__ void copy8(float* d, const float* s) {
-  *(float4*)d = *(const float4*)s;
-  *(float4*)(d + 4) = *(const float4*)(s + 4);
-}
-__device__ __forceinline__ void zero8(bf16* d) {
-  bf16x8 z;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) z[i] = (bf16)0.f;
-  *(bf16x8*)d = z;
-}
-__device__ __forceinline__ void zero8(float* d) {
-  *(float4*)d = make_float4(0.f, 0.f, 0.f, 0.f);
-  *(float4*)(d + 4) = make_float4(0.f, 0.f, 0.f, 0.f);
-}
+// 8 elements of the storage type in registers (16 bytes of bf16, 32 of float)
+template <typename T> struct Chunk8;
+template <> struct Chunk8<bf16> {
+  uint4 v;
+  __device__ __forceinline__ void load(const bf16* p) { v = *(const uint4*)p; }
+  __device__ __forceinline__ void zero() { v = make_uint4(0u, 0u, 0u, 0u); }
+  __device__ __forceinline__ void store(bf16* p) const { *(uint4*)p = v; }
+};
+template <> struct Chunk8<float> {
+  float4 a, b;
+  __device__ __forceinline__ void load(const float* p) {
+    a = *(const float4*)p;
+    b = *(const float4*)(p + 4);
+  }
+  __device__ __forceinline__ void zero() { a = b = make_float4(0.f, 0.f, 0.f, 0.f); }
+  __device__ __forceinline__ void store(float* p) const {
+    *(float4*)p = a;
+    *(float4*)(p + 4) = b;
+  }
+};
+
+// R in LDS: per distance, the four 32-dimension parts at a pitch of 36
+// floats, so the parts the four lanes of a token read start on distinct
+// banks (a pitch of 32 would put parts 0 and 2 on the same banks).
+constexpr int RPART = DPL + 4;
+constexpr int RROW = 4 * RPART;
 
 template <typename T>
 __global__ void __launch_bounds__(256) k_attn(const T* __restrict__ qkv, const float* __restrict__ R,
@@ -79,28 +90,43 @@ __global__ void __launch_bounds__(256) k_attn(const T* __restrict__ qkv, const f
   constexpr int LD = Stage<T>::LD;
   __shared__ __attribute__((aligned(16))) T Ks[ROWS * LD];
   __shared__ __attribute__((aligned(16))) T Vs[ROWS * LD];
-  __shared__ __attribute__((aligned(16))) float Rs[MAXL * HD];
+  __shared__ __attribute__((aligned(16))) float Rs[MAXL * RROW];
   const int h = blockIdx.y;
   const int64_t t0 = (int64_t)blockIdx.x * QB;
   const int tid = threadIdx.x;
   const int64_t ld = 3 * (int64_t)d;
-  // stage K and V: rows t0 - HALO .. t0 + QB - 1, 8 elements per thread-step
-  for (int idx = tid; idx < ROWS * (HD / 8); idx += 256) {
+  // stage K and V: rows t0 - HALO .. t0 + QB - 1, 8 elements per chunk; all
+  // of a thread's loads are issued before its first LDS store
+  constexpr int CH = ROWS * (HD / 8);
+  constexpr int IT = (CH + 255) / 256;
+  Chunk8<T> kc[IT], vc[IT];
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int idx = tid + it * 256;
     const int rr = idx / (HD / 8), c = (idx - rr * (HD / 8)) * 8;
     const int64_t t = t0 - HALO + rr;
-    if (t >= 0 && t < n) {
-      copy8(&Ks[rr * LD + c], qkv + t * ld + d + h * HD + c);
-      copy8(&Vs[rr * LD + c], qkv + t * ld + 2 * d + h * HD + c);
+    if (idx < CH && t >= 0 && t < n) {
+      kc[it].load(qkv + t * ld + d + h * HD + c);
+      vc[it].load(qkv + t * ld + 2 * d + h * HD + c);
     } else {
-      zero8(&Ks[rr * LD + c]);
-      zero8(&Vs[rr * LD + c]);
+      kc[it].zero();
+      vc[it].zero();
     }
   }
   for (int idx = tid; idx < MAXL * HD / 4; idx += 256) {
     const int dist = idx / (HD / 4), c = (idx - dist * (HD / 4)) * 4;
     float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
     if (dist < left) v = *(const float4*)(R + (int64_t)dist * d + h * HD + c);
-    *(float4*)&Rs[dist * HD + c] = v;
+    *(float4*)&Rs[dist * RROW + (c / DPL) * RPART + c % DPL] = v;
+  }
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int idx = tid + it * 256;
+    if (idx < CH) {
+      const int rr = idx / (HD / 8), c = (idx - rr * (HD / 8)) * 8;
+      kc[it].store(&Ks[rr * LD + c]);
+      vc[it].store(&Vs[rr * LD + c]);
+    }
   }
   __syncthreads();
 
@@ -120,7 +146,7 @@ __global__ void __launch_bounds__(256) k_attn(const T* __restrict__ qkv, const f
 #pragma unroll
   for (int dist = 0; dist < MAXL; ++dist) {
     const T* kr = &Ks[(qi + HALO - dist) * LD + c0];
-    const float* rr = &Rs[dist * HD + c0];
+    const float* rr = &Rs[dist * RROW + part * RPART];
     float acc = 0.f;
 #pragma unroll
     for (int i = 0; i < DPL; i += 8) {
@@ -133,26 +159,26 @@ __global__ void __launch_bounds__(256) k_attn(const T* __restrict__ qkv, const f
     }
     s[dist] = acc;
   }
-  // full logits in all four lanes of the token
+  // full logits in all four lanes of the token (the quad of lanes)
 #pragma unroll
-  for (int dist = 0; dist < MAXL; ++dist) {
-    s[dist] += __shfl_xor(s[dist], 1, 64);
-    s[dist] += __shfl_xor(s[dist], 2, 64);
-  }
+  for (int dist = 0; dist < MAXL; ++dist) s[dist] = quad_sum(s[dist]);
+  // soft cap: cap tanh(s / cap), tanh(x) = 1 - 2 / (e^{2x} + 1) (e^{2x}
+  // overflowing to inf gives 1, underflowing to 0 gives -1)
+  const float two_over_cap = 2.0f / cap;
   float mx = -INFINITY;
 #pragma unroll
   for (int dist = 0; dist < MAXL; ++dist) {
-    const float z = cap * tanhf(s[dist] / cap);
-    s[dist] = dist < span ? z : -INFINITY;
+    const float t = 1.0f - 2.0f * __builtin_amdgcn_rcpf(__expf(s[dist] * two_over_cap) + 1.0f);
+    s[dist] = dist < span ? cap * t : -INFINITY;
     mx = fmaxf(mx, s[dist]);
   }
   float den = 0.f;
 #pragma unroll
   for (int dist = 0; dist < MAXL; ++dist) {
-    s[dist] = dist < span ? expf(s[dist] - mx) : 0.f;
+    s[dist] = dist < span ? __expf(s[dist] - mx) : 0.f;
     den += s[dist];
   }
-  const float rden = 1.0f / den;
+  const float rden = __builtin_amdgcn_rcpf(den);
   float acc[DPL];
 #pragma unroll
   for (int i = 0; i < DPL; ++i) acc[i] = 0.f;

@@ -54,13 +54,46 @@ template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf
 __device__ __forceinline__ float clampf(float x, float lo, float hi) {
   return fminf(fmaxf(x, lo), hi);
 }
-__device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + __expf(-x)); }
+// 1 / (1 + e^-x) with the hardware reciprocal (about 1 ulp) rather than an
+// IEEE divide, which costs ten instructions; exp overflow gives 0 and 1 at
+// the ends as it should.
+__device__ __forceinline__ float sigmoidf_(float x) {
+  return __builtin_amdgcn_rcpf(1.0f + __expf(-x));
+}
+
+// Cross-lane moves within rows of 16 lanes (DPP): CTRL is the dpp_ctrl
+// field, 0x00-0xFF a permutation inside each quad of lanes, 0x140 mirrors a
+// row, 0x141 mirrors each half row.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over each quad of lanes (4 consecutive lanes); every lane of the quad
+// gets the same bits.
+__device__ __forceinline__ float quad_sum(float v) {
+  v += dpp_mov<0xB1>(v);  // quad permutation (1,0,3,2): lane ^ 1
+  v += dpp_mov<0x4E>(v);  // quad permutation (2,3,0,1): lane ^ 2
+  return v;
+}
+
+// Sum over each row of 16 lanes; every lane of the row gets the same bits
+// (each step adds a lane to its mirror image, like an xor butterfly).
+__device__ __forceinline__ float row16_sum(float v) {
+  v = quad_sum(v);
+  v += dpp_mov<0x141>(v);  // half-row mirror: quad 0 <-> 1, 2 <-> 3
+  v += dpp_mov<0x140>(v);  // row mirror: lanes 0-7 <-> 15-8
+  return v;
+}
 
 // Sum over the 64 lanes of a wavefront; every lane gets the total.
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
+  v = row16_sum(v);
+  const int b = __float_as_int(v);
+  return (__int_as_float(__builtin_amdgcn_readlane(b, 0)) +
+          __int_as_float(__builtin_amdgcn_readlane(b, 16))) +
+         (__int_as_float(__builtin_amdgcn_readlane(b, 32)) +
+          __int_as_float(__builtin_amdgcn_readlane(b, 48)));
 }
 
 // Index of the clip holding packed row `r`: the largest c with off[c] <= r,

@@ -5,8 +5,10 @@
 // layer_norm_relu). Frames past the clip's end are zeros: they are never
 // computed, and the padding treats them as absent.
 //
-// One block per output row t1 (a pair of frames): the three mel rows it
-// reads (2 t1 - 1 .. 2 t1 + 1) are staged in LDS with a zero border. A lane
+// One block per 8 consecutive output rows t1 (pairs of frames; packed, so
+// possibly across clips); for each row the three mel rows it reads
+// (2 t1 - 1 .. 2 t1 + 1) are staged in LDS with a zero border, while a
+// lane's 72 taps and 8 gains stay in registers for all 8 rows. A lane
 // owns 8 consecutive channels of one output frequency; 16 lanes cover the
 // 128 channels of a frequency, so the channel statistics are 16-lane
 // reductions and each lane writes its 8 outputs as one vector. A wavefront
@@ -17,6 +19,8 @@
 
 namespace ae {
 namespace {
+
+constexpr int kConv0Rows = 8;  // output rows per block
 
 __device__ __forceinline__ void store8(float* p, const float* v) {
   *(float4*)p = make_float4(v[0], v[1], v[2], v[3]);
@@ -33,24 +37,13 @@ template <typename T>
 __global__ void __launch_bounds__(256) k_conv0(const float* __restrict__ mel,
                                                const int64_t* __restrict__ frame_off,
                                                const int64_t* __restrict__ row_off, int B,
-                                               const float* __restrict__ w0,
+                                               int64_t total_rows, const float* __restrict__ w0,
                                                const float* __restrict__ g0, T* __restrict__ y0) {
   __shared__ float m[3][kMels + 2];
-  const int64_t r = blockIdx.x;
-  const int c = find_clip(row_off, B, r);
-  const int t1 = (int)(r - row_off[c]);
-  const int64_t fbase = frame_off[c];
-  const int F = (int)(frame_off[c + 1] - fbase);
-  for (int idx = threadIdx.x; idx < 3 * (kMels + 2); idx += 256) {
-    const int dt = idx / (kMels + 2), j = idx - dt * (kMels + 2);
-    const int ti = 2 * t1 + dt - 1, fi = j - 1;
-    float v = 0.f;
-    if (ti >= 0 && ti < F && fi >= 0 && fi < kMels) v = mel[(fbase + ti) * kMels + fi];
-    m[dt][j] = v;
-  }
-  __syncthreads();
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int fsub = lane >> 4, c0 = (lane & 15) * 8;
+  // this lane's 8 channels: 9 taps each and the LayerNorm gains, kept in
+  // registers for all the block's rows
   float wk[8][9], g[8];
 #pragma unroll
   for (int c = 0; c < 8; ++c) {
@@ -58,40 +51,56 @@ __global__ void __launch_bounds__(256) k_conv0(const float* __restrict__ mel,
     for (int k = 0; k < 9; ++k) wk[c][k] = w0[(c0 + c) * 9 + k];
     g[c] = g0[c0 + c];
   }
-#pragma unroll
-  for (int it = 0; it < 4; ++it) {
-    const int f = w * 16 + it * 4 + fsub;
-    float x[9];
-#pragma unroll
-    for (int dt = 0; dt < 3; ++dt)
-#pragma unroll
-      for (int df = 0; df < 3; ++df) x[dt * 3 + df] = m[dt][2 * f + df];  // column 2f+df-1, shifted
-    float a[8];
-    float sum = 0.f;
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      float acc = 0.f;
-#pragma unroll
-      for (int k = 0; k < 9; ++k) acc += wk[c][k] * x[k];
-      a[c] = acc;
-      sum += acc;
+  const int64_t r_first = (int64_t)blockIdx.x * kConv0Rows;
+  for (int rr = 0; rr < kConv0Rows; ++rr) {
+    const int64_t r = r_first + rr;
+    if (r >= total_rows) break;
+    const int c = find_clip(row_off, B, r);
+    const int t1 = (int)(r - row_off[c]);
+    const int64_t fbase = frame_off[c];
+    const int F = (int)(frame_off[c + 1] - fbase);
+    if (rr > 0) __syncthreads();  // the previous row's reads of m are done
+    for (int idx = threadIdx.x; idx < 3 * (kMels + 2); idx += 256) {
+      const int dt = idx / (kMels + 2), j = idx - dt * (kMels + 2);
+      const int ti = 2 * t1 + dt - 1, fi = j - 1;
+      float v = 0.f;
+      if (ti >= 0 && ti < F && fi >= 0 && fi < kMels) v = mel[(fbase + ti) * kMels + fi];
+      m[dt][j] = v;
     }
+    __syncthreads();
 #pragma unroll
-    for (int o = 8; o > 0; o >>= 1) sum += __shfl_xor(sum, o, 64);
-    const float mean = sum * (1.0f / kC0);
-    float q = 0.f;
+    for (int it = 0; it < 4; ++it) {
+      const int f = w * 16 + it * 4 + fsub;
+      float x[9];
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      a[c] -= mean;
-      q += a[c] * a[c];
+      for (int dt = 0; dt < 3; ++dt)
+#pragma unroll
+        for (int df = 0; df < 3; ++df) x[dt * 3 + df] = m[dt][2 * f + df];  // column 2f+df-1, shifted
+      float a[8];
+      float sum = 0.f;
+#pragma unroll
+      for (int cc = 0; cc < 8; ++cc) {
+        float acc = 0.f;
+#pragma unroll
+        for (int k = 0; k < 9; ++k) acc += wk[cc][k] * x[k];
+        a[cc] = acc;
+        sum += acc;
+      }
+      sum = row16_sum(sum);
+      const float mean = sum * (1.0f / kC0);
+      float q = 0.f;
+#pragma unroll
+      for (int cc = 0; cc < 8; ++cc) {
+        a[cc] -= mean;
+        q += a[cc] * a[cc];
+      }
+      q = row16_sum(q);
+      const float inv = rsqrtf(q * (1.0f / kC0) + kEps);
+      float o8[8];
+#pragma unroll
+      for (int cc = 0; cc < 8; ++cc) o8[cc] = fmaxf(a[cc] * inv * g[cc], 0.f);
+      store8(y0 + ((size_t)r * kF1 + f) * kC0 + c0, o8);
     }
-#pragma unroll
-    for (int o = 8; o > 0; o >>= 1) q += __shfl_xor(q, o, 64);
-    const float inv = rsqrtf(q * (1.0f / kC0) + kEps);
-    float o8[8];
-#pragma unroll
-    for (int c = 0; c < 8; ++c) o8[c] = fmaxf(a[c] * inv * g[c], 0.f);
-    store8(y0 + ((size_t)r * kF1 + f) * kC0 + c0, o8);
   }
 }
 
@@ -101,12 +110,13 @@ hipError_t launch_conv0(ae_dtype dt, const float* mel, const int64_t* frame_off,
                         const int64_t* row_off, int B, int64_t total_rows, const float* w0,
                         const float* g0, void* y0, hipStream_t s) {
   if (total_rows <= 0) return hipSuccess;
+  const unsigned grid = (unsigned)((total_rows + kConv0Rows - 1) / kConv0Rows);
   if (dt == AE_BF16)
-    hipLaunchKernelGGL(k_conv0<bf16>, dim3((unsigned)total_rows), dim3(256), 0, s, mel, frame_off,
-                       row_off, B, w0, g0, (bf16*)y0);
+    hipLaunchKernelGGL(k_conv0<bf16>, dim3(grid), dim3(256), 0, s, mel, frame_off, row_off, B,
+                       total_rows, w0, g0, (bf16*)y0);
   else
-    hipLaunchKernelGGL(k_conv0<float>, dim3((unsigned)total_rows), dim3(256), 0, s, mel,
-                       frame_off, row_off, B, w0, g0, (float*)y0);
+    hipLaunchKernelGGL(k_conv0<float>, dim3(grid), dim3(256), 0, s, mel, frame_off, row_off, B,
+                       total_rows, w0, g0, (float*)y0);
   return hipGetLastError();
 }
 
