@@ -32,9 +32,10 @@ PEAK_F32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
 PEAK_F64_TFLOPS = 78.6   # fp64 vector FMA: 256 CUs x 64 lanes x 2 flops x 2.4 GHz
 
-# HBM traffic per launch measured with rocprofv3 counters; valid only while
-# the kernel sources hash to what they were when the counters were taken.
-TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "traffic_batch32.md")
+# HBM traffic per launch measured with rocprofv3 counters, one record per
+# kernel class and workload (profiles/traffic_<class>_<workload>.md); valid
+# only while the kernel sources hash to what they were when the counters
+# were taken.
 KERNEL_SOURCES = {
     "logmel": ["logmel.hip", "common.h"],
     "gemm": ["gemm.hip", "launch.h", "common.h"],
@@ -71,8 +72,9 @@ def sources_sha256(kclass):
 def recorded_traffic(kclass, workload):
     """Bytes per launch from the committed counter record, or None when there
     is no record for this kernel and workload or its sources have changed."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kclass}_{workload}.md")
     try:
-        with open(TRAFFIC_RECORD) as fh:
+        with open(path) as fh:
             text = fh.read()
     except OSError:
         return None
@@ -98,6 +100,17 @@ def cpu_baseline(clip, W, seconds):
                       f"encoder in float64 numpy, {dt:.1f} s wall"}
 
 
+def copy_probe(torch):
+    """One plain device-to-device copy of COPY_PROBE_BYTES: the counters'
+    calibration under rocprofv3 --pmc."""
+    src = torch.ones(COPY_PROBE_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
+
 def bench_resample(args, torch, ae, synth):
     """32 clips x 30 s of stereo at 48 kHz -> mono 16 kHz (mixdown and the
     Kaiser-sinc resampler, float64 accumulation)."""
@@ -121,6 +134,8 @@ def bench_resample(args, torch, ae, synth):
     launches, kms = ae.timing_read()
     ae.timing_enable(None)
     ms = (t1 - t0) * 1e3 / args.steps
+    if args.copy_probe:
+        copy_probe(torch)
     audio_s = float(off[-1]) / 48000.0
     info = r.info()
     # the method's multiply-adds: the taps inside the window of every output
@@ -226,12 +241,7 @@ def main():
     ae.timing_enable(None)
     ms = (t1 - t0) * 1e3 / args.steps
     if args.copy_probe:
-        src = torch.ones(COPY_PROBE_BYTES // 4, dtype=torch.float32, device="cuda")
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+        copy_probe(torch)
     value = audio_s / (ms / 1e3)
     avg_ms = kms / max(launches, 1)
 

@@ -56,12 +56,12 @@ __global__ void __launch_bounds__(256) k_rownorm(RowNormParams p) {
     for (int i = 0; i < VPL; ++i) ss += y[i] * y[i];
     const float inv = rsqrtf(wave_sum(ss) * invd + kEps);
 #pragma unroll
-    for (int q = 0; q < NV; ++q)
+    for (int q = 0; q < NV; ++q) {
+      float w[4];
+      load4(p.w_post + q * 256 + lane * 4, w);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int c = q * 256 + lane * 4 + e;
-        x[4 * q + e] += p.scale * (y[4 * q + e] * inv * p.w_post[c]);
-      }
+      for (int e = 0; e < 4; ++e) x[4 * q + e] += p.scale * (y[4 * q + e] * inv * w[e]);
+    }
   }
   if (p.w_out) {
     float ss = 0.f;
@@ -69,12 +69,12 @@ __global__ void __launch_bounds__(256) k_rownorm(RowNormParams p) {
     for (int i = 0; i < VPL; ++i) ss += x[i] * x[i];
     const float inv = rsqrtf(wave_sum(ss) * invd + kEps);
 #pragma unroll
-    for (int q = 0; q < NV; ++q)
+    for (int q = 0; q < NV; ++q) {
+      float w[4];
+      load4(p.w_out + q * 256 + lane * 4, w);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int c = q * 256 + lane * 4 + e;
-        x[4 * q + e] = x[4 * q + e] * inv * p.w_out[c];
-      }
+      for (int e = 0; e < 4; ++e) x[4 * q + e] = x[4 * q + e] * inv * w[e];
+    }
   }
   if (p.y || p.w_out) {
 #pragma unroll
@@ -93,12 +93,12 @@ __global__ void __launch_bounds__(256) k_rownorm(RowNormParams p) {
     for (int i = 0; i < VPL; ++i) ss += x[i] * x[i];
     const float inv = rsqrtf(wave_sum(ss) * invd + kEps);
 #pragma unroll
-    for (int q = 0; q < NV; ++q)
+    for (int q = 0; q < NV; ++q) {
+      float w[4] = {1.0f, 1.0f, 1.0f, 1.0f};
+      if (p.w_next) load4(p.w_next + q * 256 + lane * 4, w);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int c = q * 256 + lane * 4 + e;
-        x[4 * q + e] = x[4 * q + e] * inv * (p.w_next ? p.w_next[c] : 1.0f);
-      }
+      for (int e = 0; e < 4; ++e) x[4 * q + e] = x[4 * q + e] * inv * w[e];
+    }
     for (int s = 0; s < p.n_out; ++s) {
       T* arow = (T*)p.a[s] + row * d;
       const float lo = p.lo[s], hi = p.hi[s];
