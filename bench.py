@@ -7,7 +7,7 @@ residual stream; random-init weights. A step is one ae_encode over the
 batch, inputs already resident in HBM. Prints one JSON line.
 
   python bench.py [--gpus 1] [--steps 20] [--warmup 5]
-                  [--workload batch32|frontend256|ragged64|resample48k]
+                  [--workload batch32|frontend256|ragged64|resample48k|merge32]
                   [--kernel gemm_ffn1] [--no-cpu-baseline] [--copy-probe]
 
 --copy-probe runs one plain 256 MiB device-to-device copy after the timed
@@ -40,6 +40,7 @@ KERNEL_SOURCES = {
     "logmel": ["logmel.hip", "common.h"],
     "gemm": ["gemm.hip", "launch.h", "common.h"],
     "resample": ["resample.hip", "launch.h", "common.h"],
+    "merge": ["placement.hip", "launch.h", "common.h"],
 }
 COPY_PROBE_BYTES = 256 << 20
 
@@ -172,13 +173,73 @@ def bench_resample(args, torch, ae, synth):
     print(json.dumps(rec), flush=True)
 
 
+def bench_merge(args, torch, ae, synth):
+    """The soft tokens of 32 inputs (750 each, 512-d) merged into their
+    text embedding rows: ids expanded on the host (ae_expand_ids), rows
+    placed on the GPU (ae_merge_soft_tokens)."""
+    rng = np.random.default_rng(7)
+    seqs = []
+    for _ in range(32):
+        body = list(rng.integers(3, 250000, 16))
+        body.insert(int(rng.integers(0, 17)), ae.RELEASE_AUDIO)
+        seqs.append(ae.expand_ids(body, [750], bos=2, eos=1, max_tokens=4096))
+    ids_np = np.concatenate(seqs)
+    L, d, S = len(ids_np), 512, 32 * 750
+    ids = torch.from_numpy(ids_np).cuda()
+    x = torch.randn((L, d), dtype=torch.float32, device="cuda")
+    soft = torch.randn((S, d), dtype=torch.float32, device="cuda")
+    step = lambda: ae.merge_soft_tokens(ids, x, soft)  # noqa: E731
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ae.timing_enable("merge")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    launches, kms = ae.timing_read()
+    ae.timing_enable(None)
+    ms = (t1 - t0) * 1e3 / args.steps
+    if args.copy_probe:
+        copy_probe(torch)
+    avg_ms = kms / max(launches, 1)
+    # algorithmic bytes: every id read once, every soft row read and written once
+    per_launch = 4.0 * L + 2.0 * 4.0 * S * d
+    achieved = per_launch / (avg_ms / 1e3) / 1e9
+    roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": achieved / PEAK_HBM_GBS,
+            "traffic": recorded_traffic("merge", args.workload), "kernel": "merge (3 kernels)",
+            "avg_ms": avg_ms, "launches": launches}
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle.placeholders as oph
+        xs, ss = x.cpu().numpy(), soft.cpu().numpy()
+        t0 = time.perf_counter()
+        oph.merge_soft_tokens(xs, ids_np, ss)
+        dt = time.perf_counter() - t0
+        cpu = {"value": S / dt, "unit": "soft tokens/s", "cores": 1, "kind": "oracle",
+               "sample": f"the whole workload through the oracle's merge (numpy rows), {dt:.2f} s"}
+    rec = {"metric": "soft tokens merged/sec (32 inputs x 750 soft tokens, 512-d)",
+           "value": S / (ms / 1e3), "unit": "soft tokens/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+           "data": "synthetic (seeded ids, random rows)",
+           "config": {"workload": "32 inputs x (16 text ids + 1 clip of 750 soft tokens), d 512: "
+                                  "soft-token merge into the embedding rows",
+                      "global_batch": 32, "ids": L, "soft_tokens": S, "parallelism": "none (1 GPU)"},
+           "roofline": roof, "cpu_baseline": cpu}
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="batch32",
-                    choices=["batch32", "frontend256", "ragged64", "resample48k"])
+                    choices=["batch32", "frontend256", "ragged64", "resample48k", "merge32"])
     ap.add_argument("--kernel", default="gemm_ffn1")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true")
@@ -196,6 +257,8 @@ def main():
     log(f"[bench] workload {args.workload}: generating inputs")
     if args.workload == "resample48k":
         return bench_resample(args, torch, ae, synth)
+    if args.workload == "merge32":
+        return bench_merge(args, torch, ae, synth)
     if args.workload == "batch32":
         clips = synth.multisine_batch(32)
     elif args.workload == "ragged64":

@@ -250,6 +250,44 @@ ae_status ae_to_mono_16k(const ae_resampler* r, const float* in, const int64_t* 
                          int32_t B, int32_t channels, float* y, void* ws, size_t ws_bytes,
                          ae_stream stream);
 
+/* --- soft-token placement (around the encoder) -------------------------
+ * The page: input_ids and embed_audio_inputs. */
+
+/* Token ids of the placement: the audio placeholder (<|audio|>, also the id
+ * of every soft-token position), the opening and closing audio markers
+ * (<|audio>, <audio|>) and the text tokenizer's BOS and EOS. The release
+ * uses audio 258881, boa 256000, eoa 258883. */
+typedef struct {
+  int32_t audio, boa, eoa, bos, eos;
+} ae_token_ids;
+
+/* Host-only expansion of one input (the page: input_ids): body (host int32
+ * [len], the tokenized text, holding one audio placeholder per clip)
+ * becomes [bos] + body + [eos] with placeholder k replaced by
+ * [boa] + n_soft[k] x [audio] + [eoa]. out: host int32 [out_cap];
+ * *out_len receives the expanded length (also when the call fails for
+ * capacity). AE_ERR_SHAPE when the body's placeholder count is not
+ * `clips`, AE_ERR_CAPACITY when the result exceeds max_tokens or out_cap. */
+ae_status ae_expand_ids(const int32_t* body, int64_t len, const int64_t* n_soft, int32_t clips,
+                        const ae_token_ids* tok, int64_t max_tokens, int32_t* out,
+                        int64_t out_cap, int64_t* out_len);
+
+/* Workspace bytes for ae_merge_soft_tokens over L ids. */
+size_t ae_merge_workspace_bytes(int64_t L);
+
+/* Merge of soft tokens into text embedding rows (the page:
+ * embed_audio_inputs): ids: device int32 [L] (expanded sequences, packed);
+ * x: device float [L][d], the rows' embeddings, updated in place: the r-th
+ * row (in order) whose id equals `audio` receives soft row r, for
+ * r < n_soft (soft: device float [n_soft][d], the encoder's output for the
+ * clips in the same order). count: device int64 (nullable) receives the
+ * number of audio rows; a caller checks it equals n_soft (the page refuses
+ * otherwise; rows past n_soft keep their values). d a multiple of 4; x and
+ * soft 16-byte aligned. */
+ae_status ae_merge_soft_tokens(const int32_t* ids, int64_t L, int32_t audio, const float* soft,
+                               int64_t n_soft, int32_t d, float* x, int64_t* count, void* ws,
+                               size_t ws_bytes, ae_stream stream);
+
 /* --- measurement ----------------------------------------------------- */
 
 /* Kernel classes the library can time with HIP events recorded on the
@@ -260,7 +298,7 @@ typedef enum {
   AE_K_LOGMEL = 0, AE_K_CONV0 = 1, AE_K_CONV1 = 2, AE_K_GEMM_FFN1 = 3,
   AE_K_GEMM_FFN2 = 4, AE_K_GEMM_QKV = 5, AE_K_GEMM_POST = 6, AE_K_GEMM_LCSTART = 7,
   AE_K_GEMM_LCEND = 8, AE_K_GEMM_HEAD = 9, AE_K_ROWNORM = 10, AE_K_ATTN = 11,
-  AE_K_LCONV = 12, AE_K_RESAMPLE = 13, AE_K_MIXDOWN = 14, AE_K_COUNT = 15
+  AE_K_LCONV = 12, AE_K_RESAMPLE = 13, AE_K_MIXDOWN = 14, AE_K_MERGE = 15, AE_K_COUNT = 16
 } ae_kernel_class;
 
 /* Process-wide: from now on, bracket every launch of kernel class `cls`

@@ -9,7 +9,8 @@ raises.
 Names follow include/ae.h: ``logmel``, ``subsample``, ``conformer_layer``,
 ``encode``, ``num_frames``, ``num_tokens``, ``plan``, ``Model``, and for the
 step ahead of the log-mel ``resampled_length``, ``Resampler``, ``mixdown``,
-``resample``, ``to_mono_16k``.
+``resample``, ``to_mono_16k``; around it ``expand_ids`` and
+``merge_soft_tokens``.
 """
 from __future__ import annotations
 
@@ -24,7 +25,7 @@ AE_OK, AE_ERR_INVALID, AE_ERR_SHAPE, AE_ERR_CAPACITY, AE_ERR_UNSUPPORTED, AE_ERR
 AE_F32, AE_BF16 = 0, 1
 KERNEL_CLASSES = ("logmel", "conv0", "conv1", "gemm_ffn1", "gemm_ffn2", "gemm_qkv", "gemm_post",
                   "gemm_lcstart", "gemm_lcend", "gemm_head", "rownorm", "attn", "lconv",
-                  "resample", "mixdown")
+                  "resample", "mixdown", "merge")
 
 
 class AeError(RuntimeError):
@@ -38,6 +39,11 @@ class Config(C.Structure):
                 ("ff", C.c_int32), ("conv_kernel", C.c_int32), ("chunk", C.c_int32),
                 ("ctx_left", C.c_int32), ("ctx_right", C.c_int32), ("softcap", C.c_float),
                 ("residual_weight", C.c_float), ("out_hidden", C.c_int32), ("out_dim", C.c_int32)]
+
+
+class TokenIds(C.Structure):
+    _fields_ = [("audio", C.c_int32), ("boa", C.c_int32), ("eoa", C.c_int32), ("bos", C.c_int32),
+                ("eos", C.c_int32)]
 
 
 class Clip(C.Structure):
@@ -102,6 +108,12 @@ def lib():
             "ae_resample": (C.c_int, [_P, _P, i64p, C.c_int32, _P, _P, C.c_size_t, _P]),
             "ae_to_mono_16k": (C.c_int, [_P, _P, i64p, C.c_int32, C.c_int32, _P, _P, C.c_size_t,
                                          _P]),
+            "ae_expand_ids": (C.c_int, [C.POINTER(C.c_int32), C.c_int64, i64p, C.c_int32,
+                                        C.POINTER(TokenIds), C.c_int64, C.POINTER(C.c_int32),
+                                        C.c_int64, i64p]),
+            "ae_merge_workspace_bytes": (C.c_size_t, [C.c_int64]),
+            "ae_merge_soft_tokens": (C.c_int, [_P, C.c_int64, C.c_int32, _P, C.c_int64, C.c_int32,
+                                               _P, _P, _P, C.c_size_t, _P]),
             "ae_timing_enable": (C.c_int, [C.c_int32]),
             "ae_timing_read": (C.c_int, [i64p, C.POINTER(C.c_double)]),
         }
@@ -409,6 +421,39 @@ def to_mono_16k(r: Resampler, x, in_off, channels: int, out=None):
     _check(lib().ae_to_mono_16k(r.handle, _ptr(x), ip, B, channels, _ptr(out), _ptr(ws),
                                 ws.numel(), _stream()))
     return out
+
+
+RELEASE_AUDIO, RELEASE_BOA, RELEASE_EOA = 258881, 256000, 258883
+
+
+def expand_ids(body, n_soft, bos, eos, max_tokens, audio=RELEASE_AUDIO, boa=RELEASE_BOA,
+               eoa=RELEASE_EOA) -> np.ndarray:
+    """Host: the placeholder expansion of one input (ae_expand_ids)."""
+    b = np.ascontiguousarray(np.asarray(body, dtype=np.int32))
+    n, npp = _i64(n_soft)
+    tok = TokenIds(audio, boa, eoa, bos, eos)
+    cap = int(len(b) + 2 + int(np.sum(n)) + len(n))
+    out = np.zeros(max(cap, 1), dtype=np.int32)
+    out_len = C.c_int64()
+    _check(lib().ae_expand_ids(b.ctypes.data_as(C.POINTER(C.c_int32)), len(b), npp, len(n),
+                               C.byref(tok), int(max_tokens),
+                               out.ctypes.data_as(C.POINTER(C.c_int32)), len(out),
+                               C.byref(out_len)))
+    return out[:out_len.value]
+
+
+def merge_soft_tokens(ids, x, soft, audio=RELEASE_AUDIO):
+    """Device, in place on x (cuda float32 [L, d]): the audio rows of ids
+    (cuda int32 [L]) take the rows of soft (cuda float32 [S, d]) in order.
+    Returns the number of audio rows (a device int64 tensor)."""
+    import torch
+    L, d = x.shape
+    ws = torch.empty(max(int(lib().ae_merge_workspace_bytes(L)), 256), dtype=torch.uint8,
+                     device=x.device)
+    count = torch.zeros(1, dtype=torch.int64, device=x.device)
+    _check(lib().ae_merge_soft_tokens(_ptr(ids), L, int(audio), _ptr(soft), soft.shape[0], d,
+                                      _ptr(x), _ptr(count), _ptr(ws), ws.numel(), _stream()))
+    return count
 
 
 def timing_enable(cls):

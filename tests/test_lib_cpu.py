@@ -128,3 +128,29 @@ def test_resampler_create_refuses_bad_rates_before_any_device_work():
         assert h.value is None
     assert L.ae_resample_workspace_bytes(4, 1000, 1) == 256
     assert L.ae_resample_workspace_bytes(4, 1000, 2) == 256 + 4096
+
+
+def test_expand_ids_matches_oracle():
+    from oracle import placeholders as ph
+    rng = np.random.default_rng(4)
+    A = ph.AUDIO_TOKEN
+    for _ in range(100):
+        k = int(rng.integers(0, 4))
+        body = list(rng.integers(3, 5000, int(rng.integers(0, 20))))
+        for _ in range(k):
+            body.insert(int(rng.integers(0, len(body) + 1)), A)
+        n = list(rng.integers(0, 800, k))
+        want = ph.expand_ids(body, n, bos=2, eos=1, max_tokens=10 ** 6)
+        got = ae.expand_ids(body, n, bos=2, eos=1, max_tokens=10 ** 6)
+        assert got.tolist() == want
+
+
+def test_expand_ids_refusals():
+    A = ae.RELEASE_AUDIO
+    with pytest.raises(ae.AeError) as e:
+        ae.expand_ids([5, A], [3, 4], bos=2, eos=1, max_tokens=100)
+    assert e.value.status == ae.AE_ERR_SHAPE
+    with pytest.raises(ae.AeError) as e:
+        ae.expand_ids([A], [98], bos=2, eos=1, max_tokens=100)
+    assert e.value.status == ae.AE_ERR_CAPACITY
+    assert len(ae.expand_ids([A], [96], bos=2, eos=1, max_tokens=100)) == 100
