@@ -7,7 +7,7 @@ residual stream; random-init weights. A step is one ae_encode over the
 batch, inputs already resident in HBM. Prints one JSON line.
 
   python bench.py [--gpus 1] [--steps 20] [--warmup 5]
-                  [--workload batch32|frontend256|ragged64|resample48k|merge32]
+                  [--workload batch32|batch32q8|frontend256|ragged64|resample48k|merge32]
                   [--kernel gemm_ffn1] [--no-cpu-baseline] [--copy-probe]
 
 --copy-probe runs one plain 256 MiB device-to-device copy after the timed
@@ -239,7 +239,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="batch32",
-                    choices=["batch32", "frontend256", "ragged64", "resample48k", "merge32"])
+                    choices=["batch32", "batch32q8", "frontend256", "ragged64", "resample48k",
+                             "merge32"])
     ap.add_argument("--kernel", default="gemm_ffn1")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true")
@@ -259,7 +260,7 @@ def main():
         return bench_resample(args, torch, ae, synth)
     if args.workload == "merge32":
         return bench_merge(args, torch, ae, synth)
-    if args.workload == "batch32":
+    if args.workload in ("batch32", "batch32q8"):
         clips = synth.multisine_batch(32)
     elif args.workload == "ragged64":
         clips = synth.ragged_batch(64)
@@ -279,9 +280,14 @@ def main():
         kclass = "logmel"
         dtype = "f32"
     else:
-        log("[bench] generating weights (12 layers, bf16)")
-        W = synth.make_weights(layers=12, bf16=True)
-        model = ae.Model(W, dtype="bf16")
+        if args.workload == "batch32q8":
+            log("[bench] generating weights (12 layers, int8 projections)")
+            W, S = synth.make_weights_q8(layers=12)
+            model = ae.Model(W, dtype="bf16", scales=S)
+        else:
+            log("[bench] generating weights (12 layers, bf16)")
+            W = synth.make_weights(layers=12, bf16=True)
+            model = ae.Model(W, dtype="bf16")
         out = torch.empty((tokens, 512), dtype=torch.float32, device="cuda")
         model.workspace(len(clips), frames, tokens)
         step = lambda: ae.encode(model, wave, so, out=out)  # noqa: E731
@@ -327,6 +333,11 @@ def main():
     cpu = None
     if not args.no_cpu_baseline and W is not None:
         log("[bench] cpu baseline: oracle on one clip")
+        if args.workload == "batch32q8":
+            # the oracle runs the widened weights bf16(float32(q) * s)
+            from oracle import quant
+            W = {**W, "layers": [{**L, **{k: quant.dequantize_rows(L[k], sc[k]) for k in sc}}
+                                 for L, sc in zip(W["layers"], S)]}
         cpu = cpu_baseline(clips[0], W, len(clips[0]) / 16000.0)
     elif not args.no_cpu_baseline:
         import oracle
@@ -343,6 +354,8 @@ def main():
 
     names = {"batch32": "32 clips x 30 s multisine+noise: log-mel, subsampler, 12 Conformer "
                         "layers, head (bf16 MFMA, fp32 accumulation and norms)",
+             "batch32q8": "32 clips x 30 s multisine+noise, the encoder with int8 projections "
+                          "(per-row scales) widened to bf16 per layer per forward",
              "ragged64": "64 clips, 1-30 s pink noise, packed ragged: full encoder, bf16",
              "frontend256": "256 clips x 30 s white noise: log-mel front end only, fp32"}
     rec = {"metric": METRIC, "value": value, "unit": "audio-s/s", "n_gpus": 1,

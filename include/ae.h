@@ -142,6 +142,26 @@ ae_status ae_model_create(const ae_config* cfg, const ae_weights* w, ae_dtype dt
                           ae_stream stream, ae_model** out);
 void ae_model_destroy(ae_model* m);
 
+/* Per-output-row scales (float32, device, one per row of the matrix) of the
+ * ten clippable projections of a layer, for a model with int8 matrices. */
+typedef struct {
+  const float *ff1_w1, *ff1_w2, *q, *k, *v, *post, *lc_start, *lc_end, *ff2_w1, *ff2_w2;
+} ae_layer_scales;
+
+/* A bf16 model whose ten clippable projections per layer (ff1_w1, ff1_w2,
+ * q, k, v, post, lc_start, lc_end, ff2_w1, ff2_w2) are int8 [out][in] with
+ * a float32 scale per output row (scales: host array of cfg.layers entries,
+ * device pointers inside). Every other weight is as for AE_BF16. Each
+ * forward widens a layer's int8 matrices to bf16(float32(q) * scale) in the
+ * workspace before the layer runs, as the quantised linear layer of the
+ * engine.py listing (hugingapi.com multimodalart/scenema-audio, _Int8Linear)
+ * dequantises per forward; the layer then computes exactly as a bf16 model
+ * holding those matrices. Weights and scales are borrowed (they must
+ * outlive the model); calls that share such a model must not overlap in
+ * time on one workspace. */
+ae_status ae_model_create_q8(const ae_config* cfg, const ae_weights* w,
+                             const ae_layer_scales* scales, ae_stream stream, ae_model** out);
+
 /* Workspace bytes needed by ae_subsample / ae_conformer_layer / ae_encode
  * for a batch of B clips with these totals (frames, tokens over the batch). */
 size_t ae_workspace_bytes(const ae_model* m, int32_t B, int64_t total_frames,
@@ -298,7 +318,8 @@ typedef enum {
   AE_K_LOGMEL = 0, AE_K_CONV0 = 1, AE_K_CONV1 = 2, AE_K_GEMM_FFN1 = 3,
   AE_K_GEMM_FFN2 = 4, AE_K_GEMM_QKV = 5, AE_K_GEMM_POST = 6, AE_K_GEMM_LCSTART = 7,
   AE_K_GEMM_LCEND = 8, AE_K_GEMM_HEAD = 9, AE_K_ROWNORM = 10, AE_K_ATTN = 11,
-  AE_K_LCONV = 12, AE_K_RESAMPLE = 13, AE_K_MIXDOWN = 14, AE_K_MERGE = 15, AE_K_COUNT = 16
+  AE_K_LCONV = 12, AE_K_RESAMPLE = 13, AE_K_MIXDOWN = 14, AE_K_MERGE = 15, AE_K_DEQUANT = 16,
+  AE_K_COUNT = 17
 } ae_kernel_class;
 
 /* Process-wide: from now on, bracket every launch of kernel class `cls`

@@ -25,7 +25,7 @@ AE_OK, AE_ERR_INVALID, AE_ERR_SHAPE, AE_ERR_CAPACITY, AE_ERR_UNSUPPORTED, AE_ERR
 AE_F32, AE_BF16 = 0, 1
 KERNEL_CLASSES = ("logmel", "conv0", "conv1", "gemm_ffn1", "gemm_ffn2", "gemm_qkv", "gemm_post",
                   "gemm_lcstart", "gemm_lcend", "gemm_head", "rownorm", "attn", "lconv",
-                  "resample", "mixdown", "merge")
+                  "resample", "mixdown", "merge", "dequant")
 
 
 class AeError(RuntimeError):
@@ -66,6 +66,13 @@ class LayerWeights(C.Structure):
     _fields_ = LAYER_FIELDS
 
 
+Q8_FIELDS = ("ff1_w1", "ff1_w2", "q", "k", "v", "post", "lc_start", "lc_end", "ff2_w1", "ff2_w2")
+
+
+class LayerScales(C.Structure):
+    _fields_ = [(n, _P) for n in Q8_FIELDS]
+
+
 class Weights(C.Structure):
     _fields_ = [("conv0", _P), ("ln0", _P), ("conv1", _P), ("ln1", _P), ("in_proj", _P),
                 ("layers", C.POINTER(LayerWeights)), ("out_proj", _P), ("out_bias", _P),
@@ -91,6 +98,8 @@ def lib():
             "ae_plan": (C.c_int, [i64p, C.c_int32, i64p, i64p, i64p, i64p]),
             "ae_model_create": (C.c_int, [C.POINTER(Config), C.POINTER(Weights), C.c_int, _P,
                                           C.POINTER(_P)]),
+            "ae_model_create_q8": (C.c_int, [C.POINTER(Config), C.POINTER(Weights),
+                                             C.POINTER(LayerScales), _P, C.POINTER(_P)]),
             "ae_model_destroy": (None, [_P]),
             "ae_workspace_bytes": (C.c_size_t, [_P, C.c_int32, C.c_int64, C.c_int64]),
             "ae_logmel_workspace_bytes": (C.c_size_t, [C.c_int32]),
@@ -196,11 +205,16 @@ class Model:
     ``weights`` is a dict as made by ``synth.make_weights`` (numpy or torch
     arrays); matrices are stored in ``dtype`` ('f32' or 'bf16'), vectors in
     float32. Shapes are checked against the configuration, naming the
-    tensor on a mismatch.
+    tensor on a mismatch. With ``scales`` (per layer, name -> float32 [out],
+    as made by ``synth.make_weights_q8``) the ten clippable projections of
+    each layer are int8 and the model is ae_model_create_q8's.
     """
 
-    def __init__(self, weights: dict, dtype: str = "bf16", device="cuda", **cfg_over):
+    def __init__(self, weights: dict, dtype: str = "bf16", device="cuda", scales=None,
+                 **cfg_over):
         import torch
+        if scales is not None and dtype != "bf16":
+            raise AeError(AE_ERR_UNSUPPORTED, "int8 projections need dtype bf16")
         self.dtype = dtype
         self.dt = AE_BF16 if dtype == "bf16" else AE_F32
         mat_t = torch.bfloat16 if dtype == "bf16" else torch.float32
@@ -209,11 +223,18 @@ class Model:
         cfg = self.cfg
         self._keep = []
 
-        def dev(x, is_mat, name, shape):
-            t = torch.as_tensor(np.asarray(x, dtype=np.float32)) if not torch.is_tensor(x) else x
+        def dev(x, is_mat, name, shape, int8=False):
+            if int8:
+                a = np.asarray(x)
+                if a.dtype != np.int8:
+                    raise AeError(AE_ERR_INVALID, f"{name}: int8 expected, got {a.dtype}")
+                t = torch.from_numpy(np.ascontiguousarray(a))
+            else:
+                t = torch.as_tensor(np.asarray(x, dtype=np.float32)) if not torch.is_tensor(x) else x
             if tuple(t.shape) != tuple(shape):
                 raise AeError(AE_ERR_SHAPE, f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
-            t = t.to(device=device, dtype=mat_t if is_mat else torch.float32).contiguous()
+            dt_ = torch.int8 if int8 else (mat_t if is_mat else torch.float32)
+            t = t.to(device=device, dtype=dt_).contiguous()
             self._keep.append(t)
             return C.c_void_p(t.data_ptr())
 
@@ -228,7 +249,9 @@ class Model:
                     lo_i, hi_i, lo_o, hi_o = L[name]
                     setattr(lw, name, Clip(lo_i, hi_i, lo_o, hi_o))
                 else:
-                    setattr(lw, name, dev(L[name], name in _MATRICES, f"layers.{i}.{name}", shapes[name]))
+                    q8 = scales is not None and name in Q8_FIELDS
+                    setattr(lw, name, dev(L[name], name in _MATRICES, f"layers.{i}.{name}",
+                                          shapes[name], int8=q8))
         W = Weights()
         W.conv0 = dev(weights["conv0"], False, "conv0", (128, 1, 3, 3))
         W.ln0 = dev(weights["ln0"], False, "ln0", (128,))
@@ -241,7 +264,17 @@ class Model:
         W.embed = dev(weights["embed"], True, "embed", (cfg.out_dim, cfg.out_hidden))
         self._w = W
         h = C.c_void_p()
-        _check(lib().ae_model_create(C.byref(cfg), C.byref(W), self.dt, _stream(), C.byref(h)))
+        if scales is None:
+            _check(lib().ae_model_create(C.byref(cfg), C.byref(W), self.dt, _stream(), C.byref(h)))
+        else:
+            self._scales = (LayerScales * cfg.layers)()
+            for i in range(cfg.layers):
+                for name in Q8_FIELDS:
+                    setattr(self._scales[i], name,
+                            dev(scales[i][name], False, f"layers.{i}.{name}.scale",
+                                (shapes[name][0],)))
+            _check(lib().ae_model_create_q8(C.byref(cfg), C.byref(W), self._scales, _stream(),
+                                            C.byref(h)))
         self.handle = h
         self._ws = None
 

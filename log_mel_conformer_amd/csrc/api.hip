@@ -26,6 +26,8 @@ struct ae_model {
   void* conv1r = nullptr;     // [32][9 * 128], model dtype
   float* dwt = nullptr;       // [layers][conv_kernel][hidden]: light-conv taps transposed
   std::vector<int> attn_nout;  // distinct input clamps among q, k, v (1..3)
+  bool q8 = false;             // int8 projections, widened per forward
+  std::vector<ae_layer_scales> scales;
 };
 
 namespace ae {
@@ -145,6 +147,36 @@ __global__ void k_conv1_reorder(const T* __restrict__ w, T* __restrict__ wr) {
   wr[co * kC0 * 9 + tap * kC0 + ci] = w[i];
 }
 
+// Widening of int8 projections: out[r][c] = bf16(float(q[r][c]) * s[r]),
+// for up to 10 matrices in one launch, 16 values per thread.
+struct DqJobs {
+  const int8_t* q[10];
+  const float* s[10];
+  bf16* out[10];
+  int cols[10];
+  int64_t first[11];  // prefix of the jobs' 16-value chunk counts
+};
+
+__global__ void k_dequant(DqJobs j) {
+  const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (g >= j.first[10]) return;
+  int k = 0;
+  while (g >= j.first[k + 1]) ++k;
+  const int64_t e = (g - j.first[k]) * 16;
+  const int64_t r = e / j.cols[k];
+  const float sc = j.s[k][r];
+  const int4 v = *(const int4*)(j.q[k] + e);
+  const int words[4] = {v.x, v.y, v.z, v.w};
+  bf16x8 o0, o1;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    o0[i] = (bf16)((float)(int8_t)(words[i / 4] >> (8 * (i & 3))) * sc);
+    o1[i] = (bf16)((float)(int8_t)(words[2 + i / 4] >> (8 * (i & 3))) * sc);
+  }
+  *(bf16x8*)(j.out[k] + e) = o0;
+  *(bf16x8*)(j.out[k] + e + 8) = o1;
+}
+
 __global__ void k_transpose_taps(const float* w, int d, int K, float* wt) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= d * K) return;
@@ -156,6 +188,12 @@ __global__ void k_transpose_taps(const float* w, int d, int K, float* wt) {
 
 hipError_t launch_transpose_taps(const float* w, int d, int K, float* wt, hipStream_t s) {
   hipLaunchKernelGGL(k_transpose_taps, dim3((d * K + 255) / 256), dim3(256), 0, s, w, d, K, wt);
+  return hipGetLastError();
+}
+
+hipError_t launch_dequant(const DqJobs& j, hipStream_t s) {
+  if (j.first[10] == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_dequant, dim3((unsigned)((j.first[10] + 255) / 256)), dim3(256), 0, s, j);
   return hipGetLastError();
 }
 
@@ -291,6 +329,7 @@ struct Ws {
   void* c = nullptr;
   float* o1 = nullptr;
   void* on = nullptr;
+  void* dq = nullptr;  // int8 models: one layer's projections widened to bf16
   size_t total = 0;
 };
 
@@ -323,6 +362,7 @@ Ws ws_layout(const ae_model* m, int B, int64_t F, int64_t T, char* base) {
   w.c = take(es * (size_t)T * d);
   w.o1 = (float*)take(sizeof(float) * (size_t)T * m->cfg.out_hidden);
   w.on = take(es * (size_t)T * m->cfg.out_hidden);
+  if (m->q8) w.dq = take(2 * (4 * (size_t)m->cfg.ff * d + 7 * d * d));
   w.total = off;
   return w;
 }
@@ -411,12 +451,40 @@ ae_status subsample_impl(const ae_model* m, const float* mel, const Plan& pl, co
 ae_status layer_impl(const ae_model* m, int l, float* h, const int32_t* pos, int64_t n,
                      const Ws& w, hipStream_t s, bool pre_done, const ae_layer_weights* next,
                      void* h_copy) {
-  const ae_layer_weights& L = m->layers[l];
   const int d = m->cfg.hidden, ff = m->cfg.ff;
   const int M = (int)n;
   const ae_dtype dt = m->dt;
   const bool lowp = dt == AE_BF16;
   if (n == 0) return AE_OK;
+  // int8 models: widen this layer's ten projections into the workspace and
+  // run the layer on the widened copies
+  ae_layer_weights Lq = m->layers[l];
+  if (m->q8) {
+    const ae_layer_weights& L0 = m->layers[l];
+    const ae_layer_scales& S = m->scales[l];
+    const void* qs[10] = {L0.ff1_w1, L0.ff1_w2, L0.q, L0.k, L0.v, L0.post, L0.lc_start, L0.lc_end,
+                          L0.ff2_w1, L0.ff2_w2};
+    const float* ss[10] = {S.ff1_w1, S.ff1_w2, S.q, S.k, S.v, S.post, S.lc_start, S.lc_end,
+                           S.ff2_w1, S.ff2_w2};
+    const int rows[10] = {ff, d, d, d, d, d, 2 * d, d, ff, d};
+    const int cols[10] = {d, ff, d, d, d, d, d, d, d, ff};
+    const void** dst[10] = {&Lq.ff1_w1, &Lq.ff1_w2, &Lq.q, &Lq.k, &Lq.v, &Lq.post, &Lq.lc_start,
+                            &Lq.lc_end, &Lq.ff2_w1, &Lq.ff2_w2};
+    DqJobs j;
+    bf16* o = (bf16*)w.dq;
+    j.first[0] = 0;
+    for (int i = 0; i < 10; ++i) {
+      j.q[i] = (const int8_t*)qs[i];
+      j.s[i] = ss[i];
+      j.out[i] = o;
+      j.cols[i] = cols[i];
+      j.first[i + 1] = j.first[i] + (int64_t)rows[i] * cols[i] / 16;
+      *dst[i] = o;
+      o += (size_t)rows[i] * cols[i];
+    }
+    AE_LAUNCH(AE_K_DEQUANT, s, launch_dequant(j, s));
+  }
+  const ae_layer_weights& L = Lq;
 
   auto ffn = [&](const float* pre, const void* w1, const ae_clip& c1, const void* w2,
                  const ae_clip& c2, bool done) -> ae_status {
@@ -615,13 +683,29 @@ ae_status ae_timing_read(int64_t* launches, double* total_ms) {
   return AE_OK;
 }
 
-ae_status ae_model_create(const ae_config* cfg, const ae_weights* w, ae_dtype dt,
-                          ae_stream stream, ae_model** out) {
+static ae_status model_create_impl(const ae_config* cfg, const ae_weights* w, ae_dtype dt,
+                                   const ae_layer_scales* scales, ae_stream stream,
+                                   ae_model** out) {
   if (!out) return set_error(AE_ERR_INVALID, "out is NULL");
   *out = nullptr;
   if (!cfg || !w) return set_error(AE_ERR_INVALID, "cfg and weights must not be NULL");
   if (dt != AE_F32 && dt != AE_BF16) return set_error(AE_ERR_INVALID, "unknown dtype");
   const ae_config& c = *cfg;
+  if (scales) {
+    if (dt != AE_BF16) return set_error(AE_ERR_UNSUPPORTED, "int8 projections need AE_BF16");
+    if (c.layers < 1 || c.layers > 256) return set_error(AE_ERR_INVALID, "layers must be in 1..256");
+    const char* sn[] = {"ff1_w1", "ff1_w2", "q", "k", "v", "post", "lc_start", "lc_end",
+                        "ff2_w1", "ff2_w2"};
+    for (int l = 0; l < c.layers; ++l) {
+      const ae_layer_scales& S = scales[l];
+      const float* sp[] = {S.ff1_w1, S.ff1_w2, S.q, S.k, S.v, S.post, S.lc_start, S.lc_end,
+                           S.ff2_w1, S.ff2_w2};
+      for (int i = 0; i < 10; ++i)
+        if (!sp[i] || ((uintptr_t)sp[i] & 3) != 0)
+          return set_error(AE_ERR_INVALID, "layer " + std::to_string(l) + ": scale of " + sn[i] +
+                                               " is NULL or misaligned");
+    }
+  }
   if (c.ctx_right != 0)
     return set_error(AE_ERR_UNSUPPORTED, "attention_context_right " + std::to_string(c.ctx_right) +
                                              " is not supported (only 0)");
@@ -681,6 +765,10 @@ ae_status ae_model_create(const ae_config* cfg, const ae_weights* w, ae_dtype dt
   ae_model* m = new ae_model();
   m->cfg = c;
   m->dt = dt;
+  if (scales) {
+    m->q8 = true;
+    m->scales.assign(scales, scales + c.layers);
+  }
   hipGetDevice(&m->device);
   m->w = *w;
   m->layers.assign(w->layers, w->layers + c.layers);
@@ -726,6 +814,20 @@ ae_status ae_model_create(const ae_config* cfg, const ae_weights* w, ae_dtype dt
   if ((e = hipStreamSynchronize(s)) != hipSuccess) return fail(e, "model tables");
   *out = m;
   return AE_OK;
+}
+
+ae_status ae_model_create(const ae_config* cfg, const ae_weights* w, ae_dtype dt,
+                          ae_stream stream, ae_model** out) {
+  return model_create_impl(cfg, w, dt, nullptr, stream, out);
+}
+
+ae_status ae_model_create_q8(const ae_config* cfg, const ae_weights* w,
+                             const ae_layer_scales* scales, ae_stream stream, ae_model** out) {
+  if (!scales) {
+    if (out) *out = nullptr;
+    return set_error(AE_ERR_INVALID, "scales must not be NULL");
+  }
+  return model_create_impl(cfg, w, AE_BF16, scales, stream, out);
 }
 
 void ae_model_destroy(ae_model* m) {

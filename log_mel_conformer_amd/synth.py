@@ -216,5 +216,37 @@ def make_weights(layers: int = 12, bf16: bool = False, clip=CLIP8) -> dict:
     return W
 
 
+Q8_MATRICES = ("ff1_w1", "ff1_w2", "q", "k", "v", "post", "lc_start", "lc_end", "ff2_w1",
+               "ff2_w2")
+
+
+def quantize_rows(w: np.ndarray):
+    """An int8 checkpoint of a matrix, as a quantised pack would hold it:
+    symmetric per output row, scale = max |w_row| / 127 (float32),
+    q = round(w / scale) clamped to +-127. (Producing the checkpoint is
+    outside the encoder; the encoder consumes q and the scales.)"""
+    w = np.asarray(w, dtype=np.float32)
+    s = (np.abs(w).max(axis=1) / 127.0).astype(np.float32)
+    s[s == 0] = 1.0
+    q = np.clip(np.rint(w / s[:, None]), -127, 127).astype(np.int8)
+    return q, s
+
+
+def make_weights_q8(layers: int = 12, clip=CLIP8):
+    """The encoder with int8 projections: the same draws as make_weights;
+    the ten clippable projections of every layer as int8 + per-row scales,
+    every other matrix bf16-rounded. Returns (weights, scales), scales a
+    list (per layer) of dicts name -> float32 [out]."""
+    W = make_weights(layers=layers, bf16=True, clip=clip)
+    Wf = make_weights(layers=layers, bf16=False, clip=clip)
+    scales = []
+    for L, Lf in zip(W["layers"], Wf["layers"]):
+        sc = {}
+        for k in Q8_MATRICES:
+            L[k], sc[k] = quantize_rows(Lf[k])
+        scales.append(sc)
+    return W, scales
+
+
 CONFIG = dict(hidden=HIDDEN, heads=HEADS, left=12, n_dist=13, kernel=KERNEL,
               softcap=50.0, residual_weight=0.5, eps=1e-6)
