@@ -13,7 +13,9 @@ EmbeddingGemma 2), cited below as "egemma2_audio.rs" with the item it
 defines; the RMS-norm form comes from the cortiq-engine 0.5.94
 ``ltxdit.rs`` page (``rms_plain`` / ``rms_w``). The same egemma2_audio.rs
 page defines the step ahead of the log-mel, mixdown and resampling to
-16 kHz (``oracle.resample``).
+16 kHz (``oracle.resample``). The second encoder, the LFM2A Conformer of
+the docs.rs source page of cera 0.5.3 (``src/model/audio_encoder_gpu.rs``),
+is ``oracle.lfm2a``.
 
 Every function is pinned by a CPU test (values the pages print, closed
 forms, invariants, library cross-checks or brute force); the one result with
@@ -29,3 +31,4 @@ from .tower import (layer_norm_relu, subsample, rms_norm, clip_linear, silu,
                     light_conv, conformer_layer, head, encode_clips,
                     tower_constants)
 from . import resample  # the module: oracle.resample.resample, .mixdown, ...
+from . import lfm2a     # the module: oracle.lfm2a.encode, .log_mel, ...
