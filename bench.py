@@ -7,7 +7,8 @@ residual stream; random-init weights. A step is one ae_encode over the
 batch, inputs already resident in HBM. Prints one JSON line.
 
   python bench.py [--gpus 1] [--steps 20] [--warmup 5]
-                  [--workload batch32|batch32q8|frontend256|ragged64|resample48k|merge32]
+                  [--workload batch32|batch32q8|frontend256|ragged64|resample48k|merge32|
+                              lfm2a32]
                   [--kernel gemm_ffn1] [--no-cpu-baseline] [--copy-probe]
 
 --copy-probe runs one plain 256 MiB device-to-device copy after the timed
@@ -233,6 +234,89 @@ def bench_merge(args, torch, ae, synth):
     print(json.dumps(rec), flush=True)
 
 
+def lfm2a_flops_per_launch(kclass, token_counts):
+    """Algorithmic flops of one launch of an LFM2A kernel class over the
+    batch: the feed-forward GEMMs are 2 T d n_ff; the attention per clip
+    and head takes q.k, (q + v).p on the t x t (query, key) pairs and
+    softmax.v, 2 t^2 head_dim each."""
+    T = float(sum(token_counts))
+    d, ff = 512, 2048
+    if kclass in ("lfm_gemm_ffn1", "lfm_gemm_ffn2"):
+        return 2.0 * T * d * ff
+    if kclass == "lfm_attn":
+        return sum(6.0 * t * t * d for t in token_counts)
+    raise SystemExit(f"bench.py: no flop count for kernel class {kclass}")
+
+
+def bench_lfm2a(args, torch, ae, synth):
+    """The LFM2A encoder (front end, stem, 17 blocks, adapter) on 32 clips
+    of 30 s; one lfm2a_encode per step."""
+    from log_mel_conformer_amd import lfm2a
+    clips = synth.multisine_batch(32)
+    wave_np, so = synth.pack(clips)
+    wave = torch.from_numpy(wave_np).cuda()
+    pl = lfm2a.plan(np.diff(so))
+    toks = [int(t) for t in np.diff(pl["token_off"])]
+    tokens, frames = int(pl["token_off"][-1]), int(pl["frame_off"][-1])
+    audio_s = float(so[-1]) / 16000.0
+    log("[bench] generating weights (LFM2A, 17 blocks, bf16)")
+    W = synth.make_lfm2a_weights(17)
+    model = lfm2a.Model(W)
+    out = torch.empty((tokens, 2048), dtype=torch.float32, device="cuda")
+    model.workspace(len(clips), frames, tokens, max(toks))
+    kclass = args.kernel if args.kernel.startswith("lfm_") else "lfm_gemm_ffn1"
+    step = lambda: lfm2a.encode(model, wave, so, out=out)  # noqa: E731
+    log(f"[bench] warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"[bench] timing {args.steps} steps (events around {kclass})")
+    ae.timing_enable(kclass)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    launches, kms = ae.timing_read()
+    ae.timing_enable(None)
+    ms = (t1 - t0) * 1e3 / args.steps
+    if args.copy_probe:
+        copy_probe(torch)
+    avg_ms = kms / max(launches, 1)
+    achieved = lfm2a_flops_per_launch(kclass, toks) / (avg_ms / 1e3) / 1e12
+    roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": achieved / PEAK_BF16_TFLOPS, "traffic": recorded_traffic(kclass, args.workload),
+            "kernel": kclass, "avg_ms": avg_ms, "launches": launches}
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline: the LFM2A oracle on one clip")
+        from oracle import lfm2a as olfm
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        c0 = time.perf_counter()
+        olfm.encode(clips[0], W)
+        dt = time.perf_counter() - c0
+        cpu = {"value": 30.0 / dt, "unit": "audio-s/s", "cores": threads, "kind": "oracle",
+               "sample": f"1 clip of the workload (30 s), the whole LFM2A encoder in float64 "
+                         f"numpy, {dt:.1f} s wall"}
+    rec = {"metric": "audio-seconds encoded/sec (LFM2A Conformer: front end, stem, 17 blocks, "
+                     "adapter; batch 32)",
+           "value": audio_s / (ms / 1e3), "unit": "audio-s/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+           "data": "synthetic (seeded waveforms, random-init weights)",
+           "config": {"workload": "32 clips x 30 s multisine+noise through the LFM2A encoder: "
+                                  "log-mel (pre-emphasis, power, Slaney, per-bin norm), 8x "
+                                  "conv stem, 17 relative-position Conformer blocks, adapter "
+                                  "to 2048 (bf16 MFMA, fp32 accumulation and norms)",
+                      "global_batch": len(clips), "seq_len": max(toks), "tokens": tokens,
+                      "frames": frames, "audio_seconds": audio_s,
+                      "tokens_per_s": tokens / (ms / 1e3), "parallelism": "none (1 GPU)"},
+           "roofline": roof, "cpu_baseline": cpu}
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -240,7 +324,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="batch32",
                     choices=["batch32", "batch32q8", "frontend256", "ragged64", "resample48k",
-                             "merge32"])
+                             "merge32", "lfm2a32"])
     ap.add_argument("--kernel", default="gemm_ffn1")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true")
@@ -260,6 +344,8 @@ def main():
         return bench_resample(args, torch, ae, synth)
     if args.workload == "merge32":
         return bench_merge(args, torch, ae, synth)
+    if args.workload == "lfm2a32":
+        return bench_lfm2a(args, torch, ae, synth)
     if args.workload in ("batch32", "batch32q8"):
         clips = synth.multisine_batch(32)
     elif args.workload == "ragged64":

@@ -319,7 +319,15 @@ typedef enum {
   AE_K_GEMM_FFN2 = 4, AE_K_GEMM_QKV = 5, AE_K_GEMM_POST = 6, AE_K_GEMM_LCSTART = 7,
   AE_K_GEMM_LCEND = 8, AE_K_GEMM_HEAD = 9, AE_K_ROWNORM = 10, AE_K_ATTN = 11,
   AE_K_LCONV = 12, AE_K_RESAMPLE = 13, AE_K_MIXDOWN = 14, AE_K_MERGE = 15, AE_K_DEQUANT = 16,
-  AE_K_COUNT = 17
+  /* the LFM2A encoder (lfm2a.h): front end (all four kernels), stem
+   * convolutions, stem pointwise GEMMs with pre_encode_out, the blocks'
+   * feed-forward GEMMs (up, down), attention GEMMs (q|k|v, linear_pos,
+   * attn_o), convolution-module GEMMs (pw1, pw2), adapter GEMMs,
+   * LayerNorms, attention, depthwise conv */
+  AE_K_LFM_FRONT = 17, AE_K_LFM_STEM = 18, AE_K_LFM_GEMM_STEM = 19, AE_K_LFM_GEMM_FFN1 = 20,
+  AE_K_LFM_GEMM_FFN2 = 21, AE_K_LFM_GEMM_ATTN = 22, AE_K_LFM_GEMM_CONV = 23,
+  AE_K_LFM_GEMM_ADAPTER = 24, AE_K_LFM_LN = 25, AE_K_LFM_ATTN = 26, AE_K_LFM_DWCONV = 27,
+  AE_K_COUNT = 28
 } ae_kernel_class;
 
 /* Process-wide: from now on, bracket every launch of kernel class `cls`

@@ -25,7 +25,10 @@ AE_OK, AE_ERR_INVALID, AE_ERR_SHAPE, AE_ERR_CAPACITY, AE_ERR_UNSUPPORTED, AE_ERR
 AE_F32, AE_BF16 = 0, 1
 KERNEL_CLASSES = ("logmel", "conv0", "conv1", "gemm_ffn1", "gemm_ffn2", "gemm_qkv", "gemm_post",
                   "gemm_lcstart", "gemm_lcend", "gemm_head", "rownorm", "attn", "lconv",
-                  "resample", "mixdown", "merge", "dequant")
+                  "resample", "mixdown", "merge", "dequant",
+                  "lfm_front", "lfm_stem", "lfm_gemm_stem", "lfm_gemm_ffn1", "lfm_gemm_ffn2",
+                  "lfm_gemm_attn", "lfm_gemm_conv", "lfm_gemm_adapter", "lfm_ln", "lfm_attn",
+                  "lfm_dwconv")
 
 
 class AeError(RuntimeError):

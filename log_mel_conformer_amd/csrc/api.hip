@@ -393,6 +393,7 @@ GemmParams gemm_params(int M, int N, int K, const void* A, int lda, const void* 
   p.ldc = ldc;
   for (int i = 0; i < 3; ++i) { p.olo[i] = -kInf; p.ohi[i] = kInf; }
   p.nlo = -kInf; p.nhi = kInf;
+  p.rscale = 1.0f;
   return p;
 }
 

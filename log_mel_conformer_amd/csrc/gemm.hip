@@ -15,7 +15,9 @@
 // clamp of a clippable linear, SiLU plus the next projection's input clamp
 // (feed-forward), the GLU of the light conv's linear_start, the light conv's
 // residual add, the output projection's bias, per-column q/k scaling, and
-// conv1's channel LayerNorm + ReLU.
+// conv1's channel LayerNorm + ReLU; for the LFM2A encoder (cera 0.5.3,
+// audio_encoder_gpu.rs), the bias adds with ReLU, SiLU or erf GELU, the
+// GLU with its bias, and the scaled residual adds of macaron_ffn.
 #include <type_traits>
 
 #include "launch.h"
@@ -66,6 +68,14 @@ __device__ __forceinline__ void store4(bf16* p, float a, float b, float c, float
   *(bf16x4*)p = v;
 }
 
+// The activations of EPI_ACT; GELU in its erf form.
+__device__ __forceinline__ float act_apply(int act, float x) {
+  if (act == ACT_RELU) return fmaxf(x, 0.0f);
+  if (act == ACT_SILU) return x * sigmoidf_(x);
+  if (act == ACT_GELU_ERF) return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f));
+  return x;
+}
+
 // Epilogue of a wavefront's tile at (row0, col0). The MFMAs take the B
 // fragment as their first operand, so each 32x32 accumulator holds the
 // transposed sub-tile: acc[i][j][v] is C at row row0 + 32 i + lane % 32 and
@@ -92,8 +102,12 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, f32x16 (&acc)[MT][
           float o[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const float a = clampf(acc[i][2 * jp][4 * g + e], lo, hi);
-            const float b = clampf(acc[i][2 * jp + 1][4 * g + e], lo, hi);
+            float a = clampf(acc[i][2 * jp][4 * g + e], lo, hi);
+            float b = clampf(acc[i][2 * jp + 1][4 * g + e], lo, hi);
+            if (p.bias) {
+              a += p.bias[col + e];
+              b += p.bias[p.glu_d + col + e];
+            }
             o[e] = a * sigmoidf_(b);
           }
           if (ok) store4(crow + col, o[0], o[1], o[2], o[3]);
@@ -147,11 +161,23 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, f32x16 (&acc)[MT][
             if (ok) store4(crow + col, o[0], o[1], o[2], o[3]);
           } else if (EPI == EPI_RESID) {
             float* hp = (float*)crow + col;
+            float o[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[e] = clampf(x[e], lo, hi);
+            if (p.bias) {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) o[e] = (o[e] + p.bias[col + e]) * p.rscale;
+            }
             if (ok) {
               const float4 hv = *(const float4*)hp;
-              store4(hp, hv.x + clampf(x[0], lo, hi), hv.y + clampf(x[1], lo, hi),
-                     hv.z + clampf(x[2], lo, hi), hv.w + clampf(x[3], lo, hi));
+              store4(hp, hv.x + o[0], hv.y + o[1], hv.z + o[2], hv.w + o[3]);
             }
+          } else if (EPI == EPI_ACT) {
+            float o[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              o[e] = act_apply(p.act, x[e] + (p.bias ? p.bias[col + e] : 0.0f));
+            if (ok) store4(crow + col, o[0], o[1], o[2], o[3]);
           } else if (EPI == EPI_BIAS) {
             const float4 bv = *(const float4*)(p.bias + col);
             if (ok) store4((float*)crow + col, x[0] + bv.x, x[1] + bv.y, x[2] + bv.z, x[3] + bv.w);
@@ -247,8 +273,12 @@ __device__ __forceinline__ void epilogue_staged(const GemmParams& p,
             float o[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              const float a = clampf(acc[i][2 * jp][4 * g + e], lo, hi);
-              const float b = clampf(acc[i][2 * jp + 1][4 * g + e], lo, hi);
+              float a = clampf(acc[i][2 * jp][4 * g + e], lo, hi);
+              float b = clampf(acc[i][2 * jp + 1][4 * g + e], lo, hi);
+              if (p.bias) {
+                a += p.bias[ocol0 + c + e];
+                b += p.bias[p.glu_d + ocol0 + c + e];
+              }
               o[e] = a * sigmoidf_(b);
             }
             put4s<TS>(srow + c * ES, o);
@@ -276,6 +306,14 @@ __device__ __forceinline__ void epilogue_staged(const GemmParams& p,
             } else if (EPI == EPI_RESID) {
 #pragma unroll
               for (int e = 0; e < 4; ++e) o[e] = clampf(acc[i][j][4 * g + e], lo, hi);
+              if (p.bias) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) o[e] = (o[e] + p.bias[col + e]) * p.rscale;
+              }
+            } else if (EPI == EPI_ACT) {
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                o[e] = act_apply(p.act, acc[i][j][4 * g + e] + (p.bias ? p.bias[col + e] : 0.0f));
             } else {  // EPI_BIAS
               const float4 bv = *(const float4*)(p.bias + col);
               o[0] = acc[i][j][4 * g] + bv.x;
@@ -727,6 +765,7 @@ hipError_t dispatch_f32(int epi, int aload, const GemmParams& p, hipStream_t s) 
     case EPI_GLU: return run<float, float, 128, 128, 2, 2, A_PLAIN, EPI_GLU>(p, s);
     case EPI_RESID: return run<float, float, 128, 128, 2, 2, A_PLAIN, EPI_RESID>(p, s);
     case EPI_BIAS: return run<float, float, 128, 128, 2, 2, A_PLAIN, EPI_BIAS>(p, s);
+    case EPI_ACT: return run<float, float, 128, 128, 2, 2, A_PLAIN, EPI_ACT>(p, s);
   }
   return hipErrorInvalidValue;
 }
@@ -763,6 +802,8 @@ hipError_t dispatch_bf16(int epi, int aload, bool out_bf16, const GemmParams& p,
       return out_bf16 ? run_bf16<EPI_GLU, bf16>(p, s) : run_bf16<EPI_GLU, float>(p, s);
     case EPI_RESID: return run_bf16<EPI_RESID, float>(p, s);
     case EPI_BIAS: return run_bf16<EPI_BIAS, float>(p, s);
+    case EPI_ACT:
+      return out_bf16 ? run_bf16<EPI_ACT, bf16>(p, s) : run_bf16<EPI_ACT, float>(p, s);
   }
   return hipErrorInvalidValue;
 }

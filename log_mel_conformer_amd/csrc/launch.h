@@ -14,8 +14,13 @@ enum EpiKind {
   EPI_GLU = 2,     // C[:, j] = a * sigmoid(b), a/b the clamped halves (TO)
   EPI_RESID = 3,   // C (float) += clamp(acc, olo, ohi)
   EPI_BIAS = 4,    // C (float) = acc + bias[col]
-  EPI_LNRELU = 5   // C = relu(LayerNorm_32(acc) * gain)  (conv1, N = 32)
+  EPI_LNRELU = 5,  // C = relu(LayerNorm_32(acc) * gain)  (conv1, N = 32)
+  EPI_ACT = 6      // C = act(acc + bias[col]) (TO), bias optional
 };
+// Activations of EPI_ACT. EPI_GLU and EPI_RESID also add bias[col] when
+// bias is set (GLU: bias[c] to a, bias[glu_d + c] to b), and EPI_RESID
+// scales what it adds by rscale.
+enum ActKind { ACT_NONE = 0, ACT_RELU = 1, ACT_SILU = 2, ACT_GELU_ERF = 3 };
 enum ALoadKind { A_PLAIN = 0, A_CONV1 = 1 };
 
 struct GemmParams {
@@ -41,6 +46,8 @@ struct GemmParams {
   const float* colscale;
   const float* bias;
   const float* gain;
+  int act;                  // EPI_ACT: an ActKind
+  float rscale;             // EPI_RESID: C += rscale * (acc + bias)
 };
 
 // dtype: AE_F32 or AE_BF16 operands; out_bf16: TO = bf16 (else float).

@@ -16,6 +16,13 @@ Workloads (16 kHz mono, t = n / 16000):
 * ``ragged_batch``   64 clips, lengths ~ U{16000..480000} (seed 12345); clip i
                      is N(0, 0.05^2) noise through the unity-DC-gain one-pole
                      lowpass y[n] = 0.95 y[n-1] + 0.05 u[n]
+* ``make_lfm2a_weights`` the LFM2A encoder (17 blocks of width 512):
+                     matrices and conv kernels N(0, 1/fan_in), linear
+                     biases 0.05 N(0, 1), LayerNorm and per-channel affine
+                     gains 1 + 0.1 N(0, 1) with biases 0.1 N(0, 1),
+                     pos_bias_u / pos_bias_v 0.1 N(0, 1); every matrix the
+                     GEMMs read (the pointwise stem kernels included) is
+                     rounded to bf16.
 * ``make_weights``   matrices and conv kernels N(0, 1/fan_in); per_dim_scale
                      N(0, 0.1) (0.1 read as the variance); norm gains
                      1 + 0.1 N(0, 1); out_proj bias 0.1 N(0, 1); every
@@ -250,3 +257,64 @@ def make_weights_q8(layers: int = 12, clip=CLIP8):
 
 CONFIG = dict(hidden=HIDDEN, heads=HEADS, left=12, n_dist=13, kernel=KERNEL,
               softcap=50.0, residual_weight=0.5, eps=1e-6)
+
+
+# ------------------------------------------------------------ LFM2A encoder
+
+LFM2A_MATRICES = ("ffn_up_w", "ffn_down_w", "attn_q_w", "attn_k_w", "attn_v_w", "attn_o_w",
+                  "linear_pos_w", "conv_pw1_w", "conv_pw2_w", "ffn_up_1_w", "ffn_down_1_w")
+
+
+def _bias(rng, n):
+    return (0.05 * rng.standard_normal(n)).astype(np.float32)
+
+
+def _shift(rng, n):
+    return (0.1 * rng.standard_normal(n)).astype(np.float32)
+
+
+def make_lfm2a_block(seed: int, d: int = 512, ff: int = 2048, kernel: int = 9) -> dict:
+    rng = np.random.default_rng(seed)
+    L = {}
+    for nm in ("ffn_norm", "ln1", "norm_conv", "ffn_norm_1", "ln2"):
+        L[nm + "_w"] = _gain(rng, d)
+        L[nm + "_b"] = _shift(rng, d)
+    for nm, (o, i) in (("ffn_up", (ff, d)), ("ffn_down", (d, ff)), ("attn_q", (d, d)),
+                       ("attn_k", (d, d)), ("attn_v", (d, d)), ("attn_o", (d, d)),
+                       ("conv_pw1", (2 * d, d)), ("conv_pw2", (d, d)), ("ffn_up_1", (ff, d)),
+                       ("ffn_down_1", (d, ff))):
+        L[nm + "_w"] = round_bf16(_mat(rng, o, i))
+        L[nm + "_b"] = _bias(rng, o)
+    L["linear_pos_w"] = round_bf16(_mat(rng, d, d))
+    L["pos_bias_u"] = _shift(rng, d)
+    L["pos_bias_v"] = _shift(rng, d)
+    L["conv_dw_w"] = (rng.standard_normal((d, kernel)) / np.sqrt(kernel)).astype(np.float32)
+    L["conv_dw_b"] = _bias(rng, d)
+    L["conv_norm_w"] = _gain(rng, d)
+    L["conv_norm_b"] = _shift(rng, d)
+    return L
+
+
+def make_lfm2a_weights(layers: int = 17) -> dict:
+    """The LFM2A encoder's parameters in the oracle's layout (oracle.lfm2a):
+    seed 777 for the stem and the adapter, 2000 + i for block i."""
+    rng = np.random.default_rng(777)
+    stem = []
+    for shape in ((256, 1, 3, 3), (256, 1, 3, 3), (256, 256, 1, 1), (256, 1, 3, 3),
+                  (256, 256, 1, 1)):
+        fan_in = shape[1] * shape[2] * shape[3]
+        w = (rng.standard_normal(shape) / np.sqrt(fan_in)).astype(np.float32)
+        if shape[1] == 256:
+            w = round_bf16(w)      # the pointwise layers run on the bf16 GEMM
+        stem.append((w, _bias(rng, shape[0])))
+    W = {"stem": stem}
+    W["pre_encode_out_w"] = round_bf16(_mat(rng, 512, 4096))
+    W["pre_encode_out_b"] = _bias(rng, 512)
+    W["adapter_norm_w"] = _gain(rng, 512)
+    W["adapter_norm_b"] = _shift(rng, 512)
+    W["adapter_up_w"] = round_bf16(_mat(rng, 2048, 512))
+    W["adapter_up_b"] = _bias(rng, 2048)
+    W["adapter_down_w"] = round_bf16(_mat(rng, 2048, 2048))
+    W["adapter_down_b"] = _bias(rng, 2048)
+    W["blocks"] = [make_lfm2a_block(2000 + i) for i in range(layers)]
+    return W

@@ -1,0 +1,176 @@
+"""GPU parity of the LFM2A encoder (cera 0.5.3, audio_encoder_gpu.rs)
+against the oracle (oracle.lfm2a), stage by stage and end to end, through
+the C ABI.
+
+Bars. The front end is float32 arithmetic (FFT, band sums, log, float64
+statistics): relative L2 error <= 1e-4 per clip. Every later stage
+computes in bf16 (matrices, GEMM operands, attention operands and
+probabilities; float32 accumulation, residual stream and norms): relative
+L2 error <= 2e-2 per clip, the bf16 bar of the final embeddings. The
+attention kernel alone, given bf16 q, k, v and table rows, rounds only
+q + u, q + v and the probabilities to bf16: relative L2 <= 1e-2. Inputs
+are the seeded synthetic workloads of log_mel_conformer_amd.synth
+(16 kHz multisine clips, random-init weights).
+"""
+import numpy as np
+import pytest
+
+from oracle import lfm2a as O
+from log_mel_conformer_amd import synth
+from _util import rel_l2, say
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # pragma: no cover
+    pytest.skip("no GPU", allow_module_level=True)
+
+from log_mel_conformer_amd import lfm2a  # noqa: E402
+
+_W = {}
+
+
+def weights(layers):
+    if layers not in _W:
+        _W[layers] = synth.make_lfm2a_weights(layers)
+    return _W[layers]
+
+
+_M = {}
+
+
+def model(layers):
+    if layers not in _M:
+        _M[layers] = lfm2a.Model(weights(layers))
+    return _M[layers]
+
+
+def clips_of(lengths, seed0=0):
+    return [synth.multisine_clip(seed0 + i, n) if n else np.zeros(0, np.float32)
+            for i, n in enumerate(lengths)]
+
+
+def cuda(x, dtype=torch.float32):
+    return torch.as_tensor(np.ascontiguousarray(x)).to("cuda", dtype)
+
+
+RAGGED = [0, 320, 1000, 16000, 24321, 48000, 5 * 16000 + 77]
+
+
+def test_logmel_ragged_batch():
+    say("[gpu] lfm2a logmel: ragged batch with an empty and a 320-sample clip")
+    clips = clips_of(RAGGED)
+    wave, so = synth.pack(clips)
+    got = lfm2a.logmel(cuda(wave), so).cpu().numpy()
+    fo = lfm2a.plan(RAGGED)["frame_off"]
+    for i, x in enumerate(clips):
+        g = got[fo[i]:fo[i + 1]]
+        if len(x) == 0:
+            assert g.shape[0] == 0
+            continue
+        want = O.log_mel(x)
+        assert g.shape == want.shape
+        assert np.all(g[-1] == 0)                         # the frame after the statistics frames
+        r = rel_l2(g, want)
+        assert r <= 1e-4, (i, r, float(np.abs(g - want).max()))
+
+
+def test_attention_kernel_ragged():
+    say("[gpu] lfm2a xl_attention alone: 10 clips of 1..376 tokens, t_max 400")
+    rng = np.random.default_rng(5)
+    ts = [1, 5, 31, 32, 33, 127, 128, 129, 200, 376]
+    n, t_max = sum(ts), 400
+    qkv = synth.round_bf16(rng.standard_normal((n, 1536)).astype(np.float32))
+    P = synth.round_bf16(rng.standard_normal((2 * t_max - 1, 512)).astype(np.float32))
+    u = (0.3 * rng.standard_normal(512)).astype(np.float32)
+    v = (0.3 * rng.standard_normal(512)).astype(np.float32)
+    to = np.concatenate([[0], np.cumsum(ts)]).astype(np.int64)
+    got = lfm2a.xl_attention(cuda(qkv, torch.bfloat16), cuda(P, torch.bfloat16), t_max, cuda(u),
+                             cuda(v), to).float().cpu().numpy()
+    for i, t in enumerate(ts):
+        q = qkv[to[i]:to[i + 1]]
+        p = P[t_max - t:t_max + t - 1]      # the clip's rows: positions t-1 .. -(t-1)
+        want = O.xl_attention(q[:, :512], q[:, 512:1024], q[:, 1024:], p, u, v, 8)
+        r = rel_l2(got[to[i]:to[i + 1]], want)
+        assert r <= 1e-2, (t, r)
+
+
+def test_stem_ragged():
+    say("[gpu] lfm2a stem: oracle features of a ragged batch through the conv stem")
+    W = weights(1)
+    m = model(1)
+    lens = [320, 1000, 16000, 40000, 0, 16001]
+    feats = [O.log_mel(x) if len(x) else np.zeros((0, 128)) for x in clips_of(lens, 40)]
+    fo = np.concatenate([[0], np.cumsum([len(f) for f in feats])]).astype(np.int64)
+    got = lfm2a.stem(m, cuda(np.concatenate(feats)), fo).cpu().numpy()
+    to = lfm2a.plan(lens)["token_off"]
+    for i, f in enumerate(feats):
+        if len(f) == 0:
+            assert to[i + 1] == to[i]
+            continue
+        want = O.conv_stem(f, W)
+        r = rel_l2(got[to[i]:to[i + 1]], want)
+        assert r <= 2e-2, (i, r)
+
+
+def test_block_ragged():
+    say("[gpu] lfm2a block: one Conformer block over 6 clips of 1..130 tokens")
+    W = weights(2)
+    m = model(2)
+    rng = np.random.default_rng(9)
+    ts = [1, 2, 9, 33, 130, 64]
+    x = rng.standard_normal((sum(ts), 512)).astype(np.float32)
+    to = np.concatenate([[0], np.cumsum(ts)]).astype(np.int64)
+    for layer in (0, 1):
+        xd = cuda(x)
+        lfm2a.block(m, layer, xd, to)
+        got = xd.cpu().numpy()
+        for i, t in enumerate(ts):
+            want = O.conformer_block(x[to[i]:to[i + 1]], W["blocks"][layer],
+                                     O.relative_pos_emb(t), 8)
+            r = rel_l2(got[to[i]:to[i + 1]], want)
+            assert r <= 2e-2, (layer, t, r)
+
+
+def test_adapter():
+    say("[gpu] lfm2a adapter: 300 rows")
+    W = weights(1)
+    x = np.random.default_rng(3).standard_normal((300, 512)).astype(np.float32)
+    got = lfm2a.adapter(model(1), cuda(x)).cpu().numpy()
+    r = rel_l2(got, O.adapter(x, W))
+    assert r <= 2e-2, r
+
+
+def test_encode_end_to_end_17_blocks():
+    say("[gpu] lfm2a encode: 17 blocks, 4 clips (empty, 0.5 s, 1.3 s, 3 s)")
+    W = weights(17)
+    lens = [0, 8000, 20800, 48000]
+    clips = clips_of(lens, 70)
+    wave, so = synth.pack(clips)
+    got = lfm2a.encode(model(17), cuda(wave), so).cpu().numpy()
+    to = lfm2a.plan(lens)["token_off"]
+    assert got.shape == (to[-1], 2048)
+    for i, x in enumerate(clips):
+        if len(x) == 0:
+            continue
+        want = O.encode(x, W)
+        r = rel_l2(got[to[i]:to[i + 1]], want)
+        say(f"[gpu]   clip {i}: {len(want)} tokens, rel L2 {r:.2e}")
+        assert r <= 2e-2, (i, r)
+
+
+def test_encode_full_batch_sampled():
+    """32 clips of 30 s, one call as the benchmark runs it; clips 0 and 31
+    against the oracle in full."""
+    say("[gpu] lfm2a encode: 32 x 30 s, clips 0 and 31 against the oracle")
+    W = weights(17)
+    clips = synth.multisine_batch(32)
+    wave, so = synth.pack(clips)
+    got = lfm2a.encode(model(17), cuda(wave), so).cpu().numpy()
+    to = lfm2a.plan([len(c) for c in clips])["token_off"]
+    assert got.shape == (32 * 376, 2048) and np.all(np.diff(to) == 376)
+    for i in (0, 31):
+        want = O.encode(clips[i], W)
+        r = rel_l2(got[to[i]:to[i + 1]], want)
+        say(f"[gpu]   clip {i}: rel L2 {r:.2e}")
+        assert r <= 2e-2, (i, r)

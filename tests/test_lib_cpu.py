@@ -1,5 +1,5 @@
 """CPU checks of the C-ABI library: it loads, exports every symbol
-include/ae.h declares, its host-only functions agree bit-exactly with the
+include/ae.h and include/lfm2a.h declare, its host-only functions agree bit-exactly with the
 oracle's integer functions, and argument errors are reported before any
 device work (no call here touches a GPU)."""
 import ctypes as C
@@ -16,15 +16,19 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
 def _declared():
-    src = open(os.path.join(ROOT, "include", "ae.h")).read()
-    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(ae_[a-z_0-9]+)\s*\(", src)))
+    names = set()
+    inc = os.path.join(ROOT, "include")
+    for h in sorted(os.listdir(inc)):
+        if h.endswith(".h"):
+            src = re.sub(r"/\*.*?\*/", "", open(os.path.join(inc, h)).read(), flags=re.S)
+            names |= set(re.findall(r"\b((?:ae|lfm2a)_[a-z_0-9]+)\s*\(", src))
+    return sorted(names)
 
 
 def test_library_exports_every_declared_symbol():
     L = ae.lib()
     names = _declared()
-    assert len(names) >= 15, names
+    assert len(names) >= 30 and "lfm2a_encode" in names, names
     for n in names:
         assert hasattr(L, n), n
 
