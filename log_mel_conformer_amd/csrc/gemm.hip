@@ -771,12 +771,22 @@ hipError_t dispatch_f32(int epi, int aload, const GemmParams& p, hipStream_t s) 
 }
 
 // bf16 operands: direct-to-LDS pipelined kernels; the tile shape follows
-// the output width (tiles per wave of 256 CUs) and the depth of K.
+// the row count, the output width (tiles per wave of 256 CUs) and the depth
+// of K.
 //  wide   (N % 256 == 0, N >= 2048): 256x256, 8 wavefronts of 128x64, two 128-byte stages
 //  deep   (K >= 2048, N % 256 == 0): 192x256, 4 wavefronts of 96x128
 //  narrow (otherwise):               256x128, 8 wavefronts of 64x64, two blocks per CU
 template <int EPI, typename TO>
 hipError_t run_bf16(const GemmParams& p, hipStream_t s) {
+  // fewer rows (the LFM2A encoder's 12032 tokens): the shapes below leave
+  // CUs idle (a 512-column output in 192x256 tiles is 126 tiles for 256
+  // CUs). Measured inside that encoder: 256x128 tiles, two blocks per CU,
+  // for outputs of 2048 columns or more, else 128x128 tiles (four
+  // wavefronts of 64x64, three blocks per CU)
+  if (p.M < 16384) {
+    if (p.N >= 2048) return run_dl<bf16, TO, 256, 128, 4, 2, 64, 3, EPI, 2, 2>(p, s);
+    return run_dl<bf16, TO, 128, 128, 2, 2, 64, 3, EPI, 3, 4>(p, s);
+  }
   // measured inside the encoder (24000 rows): 256x256 tiles in bands of 4
   // row tiles for the wide projections, 192x256 with two blocks per CU for
   // the deep one, two 256x128 blocks per CU for the square ones

@@ -199,10 +199,8 @@ ae_status run_front(const float* wave, const Geometry& G, const Bufs& b, float* 
 ae_status run_stem(const lfm2a_model* m, const float* feat, const Geometry& G, const Bufs& b,
                    float* x, hipStream_t s) {
   const lfm2a_weights& w = m->w;
-  LFM_LAUNCH(AE_K_LFM_STEM, s, launch_stem0(feat, b.fo, b.r1, G.B, G.R1(), w.stem_w[0],
-                                            w.stem_b[0], b.y1, s));
-  LFM_LAUNCH(AE_K_LFM_STEM, s, launch_dw3s2(b.y1, b.r1, b.r2, G.B, G.R2(), lfm::kF1, m->stem_dwt[0],
-                                            w.stem_b[1], b.y2, s));
+  LFM_LAUNCH(AE_K_LFM_STEM, s, launch_stem01(feat, b.fo, b.r1, b.r2, G.B, G.R2(), w.stem_w[0],
+                                             w.stem_b[0], m->stem_dwt[0], w.stem_b[1], b.y2, s));
   {  // pointwise layer 2 + ReLU: y2 -> y3 (in y1's place)
     GemmParams p = gp((int)(G.R2() * lfm::kF2), kStemCh, kStemCh, b.y2, m->stem_pw[0], b.y1);
     p.bias = w.stem_b[2];

@@ -20,9 +20,10 @@
 // entries out of the ring along the diagonal. The table rows a wavefront
 // needs at step s are the ones wavefront w - 1 needed at step s - 1, so
 // the block loads one new 32-row tile of p per step into an NW-slot ring.
-// Softmax probabilities feed the value product straight from registers:
-// the key order inside each MFMA k-block is the one the lane already
-// holds, and the transposed V tile is read in that same order.
+// A step's K, V and p tiles are fetched into registers during the step
+// before it. Softmax probabilities feed the value product straight from
+// registers: the key order inside each MFMA k-block is the one the lane
+// already holds, and the transposed V tile is read in that same order.
 #include <math.h>
 
 #include "lfm2a_launch.h"
@@ -111,9 +112,42 @@ __global__ void __launch_bounds__(NW * 64, 2) k_xl_attention(
           make_float4(acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]);
   };
 
+  // the K, V and p tiles of a step, fetched into registers one step ahead
+  // (the loads fly while the previous step computes) and then stored to LDS
+  bf16x8 kreg, preg;
+  bf16x4 va, vb;
+  auto fetch = [&](int s) {
+    const int kr = tid >> 3, kc = (tid & 7) * 8;
+    const int j = s * KT + kr;
+    kreg = bf16x8{};
+    if (j < t) kreg = *(const bf16x8*)(qkv + (t0 + j) * ld + kD + head * kHd + kc);
+    const int vp = tid >> 4, vd = (tid & 15) * 4;
+    const int ja = s * KT + 2 * vp;
+    va = bf16x4{};
+    vb = bf16x4{};
+    if (ja < t) va = *(const bf16x4*)(qkv + (t0 + ja) * ld + 2 * kD + head * kHd + vd);
+    if (ja + 1 < t) vb = *(const bf16x4*)(qkv + (t0 + ja + 1) * ld + 2 * kD + head * kHd + vd);
+    const int64_t rho = t_max - i0 + 32 * (int64_t)s + kr;
+    preg = bf16x8{};
+    if (rho >= 0 && rho < p_rows) preg = *(const bf16x8*)(P + rho * kD + head * kHd + kc);
+  };
+  auto stage = [&](int s) {
+    const int kr = tid >> 3, kc = (tid & 7) * 8;
+    *(bf16x8*)(&Ks[kr * KP + kc]) = kreg;
+    *(bf16x8*)(&Ps[s % NW][kr * KP + kc]) = preg;
+    const int vp = tid >> 4, vd = (tid & 15) * 4;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+      const bf16x2 pr = {va[e], vb[e]};
+      *(bf16x2*)(&Vt[(vd + e) * VP + 2 * vp]) = pr;
+    }
+  };
+
   // prologue: the NW tiles before step 0's; each wavefront's first G slot
 #pragma unroll
   for (int m = -NW; m < 0; ++m) load_p(m);
+  fetch(0);
   __syncthreads();
   compute_g(-w - 1, 0);
 
@@ -123,43 +157,44 @@ __global__ void __launch_bounds__(NW * 64, 2) k_xl_attention(
   const int nsteps = (t + KT - 1) / KT;
   for (int s = 0; s < nsteps; ++s) {
     __syncthreads();  // every read of the previous K, V and the p slot reused below is done
-    {
-      const int kr = tid >> 3, kc = (tid & 7) * 8;
-      const int j = s * KT + kr;
-      bf16x8 kv = {};
-      if (j < t) kv = *(const bf16x8*)(qkv + (t0 + j) * ld + kD + head * kHd + kc);
-      *(bf16x8*)(&Ks[kr * KP + kc]) = kv;
-      const int vp = tid >> 4, vd = (tid & 15) * 4;
-      const int ja = s * KT + 2 * vp;
-      bf16x4 a = {}, b = {};
-      if (ja < t) a = *(const bf16x4*)(qkv + (t0 + ja) * ld + 2 * kD + head * kHd + vd);
-      if (ja + 1 < t) b = *(const bf16x4*)(qkv + (t0 + ja + 1) * ld + 2 * kD + head * kHd + vd);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-        const bf16x2 pr = {a[e], b[e]};
-        *(bf16x2*)(&Vt[(vd + e) * VP + 2 * vp]) = pr;
-      }
-      load_p(s);
-    }
+    stage(s);
+    if (s + 1 < nsteps) fetch(s + 1);
     __syncthreads();
-    compute_g(s - w, (s + 1) & 1);
-    lds_sync_wave();
-
-    f32x16 sacc = {};
+    // G for this step's new table tile and S for its keys: two independent
+    // MFMA chains, interleaved
+    f32x16 gacc = {}, sacc = {};
+    {
+      const bf16* pt = Ps[(s - w + NW) % NW];
 #pragma unroll
-    for (int k = 0; k < 4; ++k)
-      sacc = mfma16(*(const bf16x8*)(&Ks[ii * KP + 16 * k + 8 * hh]), qu[k], sacc);
+      for (int k = 0; k < 4; ++k) {
+        gacc = mfma16(*(const bf16x8*)(pt + ii * KP + 16 * k + 8 * hh), qv[k], gacc);
+        sacc = mfma16(*(const bf16x8*)(&Ks[ii * KP + 16 * k + 8 * hh]), qu[k], sacc);
+      }
+      float* gd = &Gs[w][(s + 1) & 1][ii * GP];
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        *(float4*)(gd + g * 8 + 4 * hh) =
+            make_float4(gacc[4 * g], gacc[4 * g + 1], gacc[4 * g + 2], gacc[4 * g + 3]);
+    }
+    lds_sync_wave();
+    // this lane's 16 (query, key) entries of G along the diagonal: all
+    // addresses are inside the ring, so every read is issued before the
+    // key mask is applied
     const float* gA = &Gs[w][s & 1][ii * GP];
     const float* gB = &Gs[w][(s + 1) & 1][ii * GP];
+    float g[16];
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int o = (v >> 2) * 8 + 4 * hh + (v & 3) - ii + 31;
+      g[v] = *(o < 32 ? gA + o : gB + (o - 32));
+    }
     float x[16];
     float mx = -INFINITY;
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const int jj = (v >> 2) * 8 + 4 * hh + (v & 3);
-      const int o = jj - ii + 31;
-      const float g = o < 32 ? gA[o] : gB[o - 32];
-      x[v] = (s * KT + jj < t) ? (sacc[v] + g) * kScaleLog2 : -INFINITY;
+      // the mask as an addend keeps every G value live (no guarded reads)
+      x[v] = fmaf(sacc[v] + g[v], kScaleLog2, s * KT + jj < t ? 0.0f : -INFINITY);
       mx = fmaxf(mx, x[v]);
     }
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
@@ -180,9 +215,9 @@ __global__ void __launch_bounds__(NW * 64, 2) k_xl_attention(
       pf[v >> 3][v & 7] = (bf16)p;
     }
 #pragma unroll
-    for (int dt = 0; dt < 2; ++dt)
+    for (int k = 0; k < 2; ++k)
 #pragma unroll
-      for (int k = 0; k < 2; ++k) {
+      for (int dt = 0; dt < 2; ++dt) {  // the two output chains alternate
         const bf16* vr = &Vt[(32 * dt + ii) * VP + 16 * k + 4 * hh];
         const u32x2 lo = *(const u32x2*)vr, hi = *(const u32x2*)(vr + 8);
         typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));

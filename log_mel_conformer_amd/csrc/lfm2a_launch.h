@@ -41,11 +41,14 @@ hipError_t launch_mel_norm(float* mel, const int64_t* sample_off, const int64_t*
                            int64_t total_frames, const float* stats, hipStream_t s);
 
 // ------------------------------------------------------------------ stem
-// layer 0: 3x3 stride 2 pad 1, 1 -> 256 channels, + bias, ReLU.
-// feat [frames][128] float -> y1 [rows1][64][256] bf16 (channels last)
-hipError_t launch_stem0(const float* feat, const int64_t* frame_off, const int64_t* row1_off,
-                        int B, int64_t rows1, const float* w0, const float* b0, bf16* y1,
-                        hipStream_t s);
+// layers 0 and 1 in one pass: 3x3 stride 2 pad 1, 1 -> 256 channels, +
+// bias, ReLU, then depthwise 3x3 stride 2 pad 1 + bias. feat [frames][128]
+// float -> y2 [rows2][32][256] bf16 (channels last); wt1: layer 1's taps
+// [9][256]
+hipError_t launch_stem01(const float* feat, const int64_t* frame_off, const int64_t* row1_off,
+                         const int64_t* row2_off, int B, int64_t rows2, const float* w0,
+                         const float* b0, const float* wt1, const float* b1, bf16* y2,
+                         hipStream_t s);
 // depthwise 3x3 stride 2 pad 1 + bias on channels-last planes:
 // y [rows_in][w_in][256] -> z [rows_out][w_in / 2][256]; wt: taps [9][256]
 hipError_t launch_dw3s2(const bf16* y, const int64_t* in_off, const int64_t* out_off, int B,

@@ -19,53 +19,108 @@ namespace {
 
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
-// ------------------------------------------------------------ stem layer 0
-// One block per output row (time step) of one clip: its three input rows
-// staged in LDS with the zero border, thread = 4 channels x 16
-// frequencies; every wavefront reads the same input taps (LDS broadcast).
-__global__ void __launch_bounds__(256) k_stem0(const float* __restrict__ feat,
-                                               const int64_t* __restrict__ frame_off,
-                                               const int64_t* __restrict__ row1_off, int B,
-                                               const float* __restrict__ w0,
-                                               const float* __restrict__ b0,
-                                               bf16* __restrict__ y1) {
-  __shared__ float in[3][kMel + 2];
+// ------------------------------------------------ stem layers 0 and 1
+// Layer 0 (3x3 stride 2, 1 -> 256 channels, ReLU) feeds only layer 1
+// (depthwise 3x3 stride 2), so one kernel makes layer 1's output straight
+// from the features and layer 0's 1.5 GB plane (at 32 x 30 s) never
+// reaches memory. One block per layer-1 output row r (time step): the
+// seven feature rows 4r - 3 .. 4r + 3 that layer 0's rows 2r - 1 .. 2r + 1
+// read sit in LDS with the zero border; lane = 4 channels, wavefront = 8
+// of the 32 output frequencies. A lane computes its channels' layer-0
+// values column by column (float32, kept in registers: column 2f + 1 of
+// one output is column 2(f + 1) - 1 of the next) and applies layer 1's
+// taps. Layer 0 values outside its plane are layer 1's zero padding.
+__global__ void __launch_bounds__(256) k_stem01(const float* __restrict__ feat,
+                                                const int64_t* __restrict__ frame_off,
+                                                const int64_t* __restrict__ row1_off,
+                                                const int64_t* __restrict__ row2_off, int B,
+                                                const float* __restrict__ w0,
+                                                const float* __restrict__ b0,
+                                                const float* __restrict__ wt1,
+                                                const float* __restrict__ b1,
+                                                bf16* __restrict__ y2) {
+  __shared__ float in[7][kMel + 2];
   const int64_t r = blockIdx.x;
-  const int c = find_clip(row1_off, B, r);
-  const int64_t rl = r - row1_off[c];
+  const int c = find_clip(row2_off, B, r);
+  const int64_t rl = r - row2_off[c];
   const int64_t F = frame_off[c + 1] - frame_off[c];
+  const int64_t H1 = row1_off[c + 1] - row1_off[c];
   const float* fc = feat + frame_off[c] * kMel;
-  for (int i = threadIdx.x; i < 3 * (kMel + 2); i += 256) {
-    const int dy = i / (kMel + 2), col = i % (kMel + 2) - 1;
-    const int64_t fr = 2 * rl + dy - 1;
-    in[dy][col + 1] = (fr >= 0 && fr < F && col >= 0 && col < kMel) ? fc[fr * kMel + col] : 0.f;
+  for (int i = threadIdx.x; i < 7 * (kMel + 2); i += 256) {
+    const int a = i / (kMel + 2), col = i % (kMel + 2) - 1;
+    const int64_t fr = 4 * rl - 3 + a;
+    in[a][col + 1] = (fr >= 0 && fr < F && col >= 0 && col < kMel) ? fc[fr * kMel + col] : 0.f;
   }
-  const int cq = threadIdx.x & 63, fg = threadIdx.x >> 6;
-  float w[4][9], b[4];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int ch = 4 * lane;
+  float w[4][9], b[4], wd[4][9], bd[4];
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    b[k] = b0[4 * cq + k];
+    b[k] = b0[ch + k];
+    bd[k] = b1[ch + k];
 #pragma unroll
-    for (int t = 0; t < 9; ++t) w[k][t] = w0[(4 * cq + k) * 9 + t];
+    for (int t = 0; t < 9; ++t) {
+      w[k][t] = w0[(ch + k) * 9 + t];
+      wd[k][t] = wt1[t * kStemCh + ch + k];
+    }
+  }
+  // which of layer 0's rows 2r - 1, 2r, 2r + 1 exist in this clip
+  bool rok[3];
+#pragma unroll
+  for (int dy = 0; dy < 3; ++dy) {
+    const int64_t rho = 2 * rl - 1 + dy;
+    rok[dy] = rho >= 0 && rho < H1;
   }
   __syncthreads();
-  bf16* out = y1 + (r * kF1) * kStemCh + 4 * cq;
-  for (int f = fg * 16; f < fg * 16 + 16; ++f) {
-    float x[9];
+  // layer-0 column f1 >= 0 (rows dy = 0..2, 4 channels); rows outside the
+  // plane are 0
+  auto column = [&](int f1, float (&v)[3][4]) {
+#pragma unroll
+    for (int dy = 0; dy < 3; ++dy) {
+      float x[9];
+#pragma unroll
+      for (int a = 0; a < 3; ++a)
+#pragma unroll
+        for (int bb = 0; bb < 3; ++bb) x[a * 3 + bb] = in[2 * dy + a][2 * f1 + bb];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        float acc = b[k];
+#pragma unroll
+        for (int t = 0; t < 9; ++t) acc += w[k][t] * x[t];
+        v[dy][k] = rok[dy] ? fmaxf(acc, 0.f) : 0.f;
+      }
+    }
+  };
+  const int f_lo = wv * 8;
+  float cprev[3][4], c0[3][4], c1[3][4];
+  if (f_lo > 0) {
+    column(2 * f_lo - 1, cprev);
+  } else {  // column -1: layer 1's zero padding
 #pragma unroll
     for (int dy = 0; dy < 3; ++dy)
 #pragma unroll
-      for (int dz = 0; dz < 3; ++dz) x[dy * 3 + dz] = in[dy][2 * f + dz];  // column 2f + dz - 1
+      for (int k = 0; k < 4; ++k) cprev[dy][k] = 0.f;
+  }
+  bf16* out = y2 + (r * kF2) * kStemCh + ch;
+  for (int f = f_lo; f < f_lo + 8; ++f) {
+    column(2 * f, c0);
+    column(2 * f + 1, c1);
     float o[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      float acc = b[k];
+      float acc = bd[k];
 #pragma unroll
-      for (int t = 0; t < 9; ++t) acc += w[k][t] * x[t];
-      o[k] = fmaxf(acc, 0.f);
+      for (int dy = 0; dy < 3; ++dy)
+        acc += wd[k][dy * 3] * cprev[dy][k] + wd[k][dy * 3 + 1] * c0[dy][k] +
+               wd[k][dy * 3 + 2] * c1[dy][k];
+      o[k] = acc;
     }
     const bf16x4 v = {(bf16)o[0], (bf16)o[1], (bf16)o[2], (bf16)o[3]};
     *(bf16x4*)(out + (size_t)f * kStemCh) = v;
+#pragma unroll
+    for (int dy = 0; dy < 3; ++dy)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) cprev[dy][k] = c1[dy][k];
   }
 }
 
@@ -309,12 +364,13 @@ unsigned grid_for(int64_t n, int per_block, unsigned cap = 65536) {
 
 }  // namespace
 
-hipError_t launch_stem0(const float* feat, const int64_t* frame_off, const int64_t* row1_off,
-                        int B, int64_t rows1, const float* w0, const float* b0, bf16* y1,
-                        hipStream_t s) {
-  if (rows1 <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_stem0, dim3((unsigned)rows1), dim3(256), 0, s, feat, frame_off, row1_off, B,
-                     w0, b0, y1);
+hipError_t launch_stem01(const float* feat, const int64_t* frame_off, const int64_t* row1_off,
+                         const int64_t* row2_off, int B, int64_t rows2, const float* w0,
+                         const float* b0, const float* wt1, const float* b1, bf16* y2,
+                         hipStream_t s) {
+  if (rows2 <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_stem01, dim3((unsigned)rows2), dim3(256), 0, s, feat, frame_off, row1_off,
+                     row2_off, B, w0, b0, wt1, b1, y2);
   return hipGetLastError();
 }
 
