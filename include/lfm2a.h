@@ -135,7 +135,8 @@ ae_status lfm2a_logmel(const float* wave, const int64_t* sample_off, int32_t B, 
 /* Validate the configuration and build the model's own tables on the
  * current device (bf16 copies of the pointwise stem weights, the
  * projection input columns reordered to the channels-last flatten, the
- * transposed depthwise stem taps, the concatenated q|k|v biases). Only
+ * transposed depthwise taps of the stem and of every block's convolution
+ * module, the concatenated q|k|v biases). Only
  * dtype AE_BF16 is implemented (bf16 matrices and MFMA operands, float32
  * accumulation, residual stream, norms and softmax). On error *out is
  * NULL. */

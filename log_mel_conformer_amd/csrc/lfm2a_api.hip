@@ -30,6 +30,7 @@ struct lfm2a_model {
   float* stem_dwt[2] = {nullptr, nullptr};  // stem layers 1 and 3, taps [9][256]
   bf16* pre_w = nullptr;                    // pre_encode_out, columns in (freq, channel) order
   float* qkv_b = nullptr;                   // [n_layer][3 * 512]
+  float* dw_t = nullptr;                    // conv-module taps transposed, [n_layer][k][512]
 };
 
 namespace {
@@ -289,7 +290,8 @@ ae_status run_block(const lfm2a_model* m, int layer, const Geometry& G, const Bu
     p.bias = L.conv_pw1_b;
     LFM_LAUNCH(AE_K_LFM_GEMM_CONV, s, launch_gemm(AE_BF16, EPI_GLU, A_PLAIN, true, p, s));
   }
-  LFM_LAUNCH(AE_K_LFM_DWCONV, s, launch_dwconv(b.g, b.tok_pos, b.tok_clip, b.to, T, L.conv_dw_w,
+  LFM_LAUNCH(AE_K_LFM_DWCONV, s, launch_dwconv(b.g, b.tok_pos, b.tok_clip, b.to, T,
+                                               m->dw_t + (size_t)layer * m->cfg.conv_kernel * kD,
                                                m->cfg.conv_kernel, L.conv_dw_b, L.conv_norm_w,
                                                L.conv_norm_b, b.c, s));
   {
@@ -458,7 +460,8 @@ ae_status lfm2a_model_create(const lfm2a_config* cfg, const lfm2a_weights* w, ae
   const size_t dwt_bytes = al256(sizeof(float) * 9 * kStemCh);
   const size_t pre_bytes = al256(2 * (size_t)kD * kFeat);
   const size_t qkvb_bytes = al256(sizeof(float) * 3 * kD * (size_t)cfg->n_layer);
-  const size_t total = 2 * pw_bytes + 2 * dwt_bytes + pre_bytes + qkvb_bytes;
+  const size_t dwl_bytes = al256(sizeof(float) * kD * (size_t)cfg->conv_kernel * cfg->n_layer);
+  const size_t total = 2 * pw_bytes + 2 * dwt_bytes + pre_bytes + qkvb_bytes + dwl_bytes;
   if (hipMalloc(&m->alloc, total) != hipSuccess) {
     m->alloc = nullptr;
     return fail(set_error(AE_ERR_HIP, "lfm2a_model_create: hipMalloc of the model tables failed"));
@@ -469,7 +472,8 @@ ae_status lfm2a_model_create(const lfm2a_config* cfg, const lfm2a_weights* w, ae
   m->stem_dwt[0] = (float*)p; p += dwt_bytes;
   m->stem_dwt[1] = (float*)p; p += dwt_bytes;
   m->pre_w = (bf16*)p; p += pre_bytes;
-  m->qkv_b = (float*)p;
+  m->qkv_b = (float*)p; p += qkvb_bytes;
+  m->dw_t = (float*)p;
   hipError_t e = launch_f32_to_bf16(w->stem_w[2], m->stem_pw[0], (int64_t)kStemCh * kStemCh, s);
   if (e == hipSuccess)
     e = launch_f32_to_bf16(w->stem_w[4], m->stem_pw[1], (int64_t)kStemCh * kStemCh, s);
@@ -477,9 +481,13 @@ ae_status lfm2a_model_create(const lfm2a_config* cfg, const lfm2a_weights* w, ae
   if (e == hipSuccess) e = launch_transpose_f32(w->stem_w[3], kStemCh, 9, m->stem_dwt[1], s);
   if (e == hipSuccess)
     e = launch_flatten_permute((const bf16*)w->pre_encode_out_w, kD, kStemCh, kF3, m->pre_w, s);
-  for (int l = 0; l < cfg->n_layer && e == hipSuccess; ++l)
+  for (int l = 0; l < cfg->n_layer && e == hipSuccess; ++l) {
     e = launch_concat3(m->blocks[l].attn_q_b, m->blocks[l].attn_k_b, m->blocks[l].attn_v_b, kD,
                        m->qkv_b + (size_t)l * 3 * kD, s);
+    if (e == hipSuccess)
+      e = launch_transpose_f32(m->blocks[l].conv_dw_w, kD, cfg->conv_kernel,
+                               m->dw_t + (size_t)l * cfg->conv_kernel * kD, s);
+  }
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   if (e != hipSuccess)
     return fail(set_error(AE_ERR_HIP, std::string("lfm2a_model_create: ") + hipGetErrorString(e)));

@@ -132,7 +132,11 @@ __global__ void __launch_bounds__(256) k_lfm_logmel(const float* __restrict__ wa
   float2* T = xbuf[fl];
   float* M = (float*)xbuf[fl];
   // windowed pre-emphasised samples of the frame the block handles next
-  // (register double buffer): lane j holds samples 2 (16 m + j) + e
+  // (register double buffer): lane j holds samples n = 2 (16 m + j) + e.
+  // Each sample is loaded once: y[s] = x[s] - 0.97 x[s - 1] takes x[s - 1]
+  // of an odd n from the same lane and of an even n from lane j - 1 of the
+  // frame's 16 (a DPP rotation within the row; lane 0 takes lane 15's
+  // previous m, and for n = 0 loads the sample before the frame itself).
   float yw[32];
   auto fetch = [&](int64_t g0) {
     const int64_t g = g0 + fl;
@@ -144,19 +148,28 @@ __global__ void __launch_bounds__(256) k_lfm_logmel(const float* __restrict__ wa
       len = (lds_off ? soff[c + 1] : sample_off[c + 1]) - start;
       base = (g - (lds_off ? foff[c] : frame_off[c])) * kHop - kCenterPad;
     }
+    auto in_clip = [&](int64_t s) { return active && s >= 0 && s < len; };
+    float x0[16], x1[16];
 #pragma unroll
-    for (int m = 0; m < 16; ++m)
+    for (int m = 0; m < 16; ++m) {
+      const int64_t s0 = base + 2 * (16 * m + j);
+      x0[m] = in_clip(s0) ? wave[start + s0] : 0.f;
+      x1[m] = in_clip(s0 + 1) ? wave[start + s0 + 1] : 0.f;
+    }
+    const float before = (j == 0 && in_clip(base - 1)) ? wave[start + base - 1] : 0.f;
+    float rot_prev = 0.f;
 #pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const int n = 2 * (16 * m + j) + e;
-        const int64_t s = base + n;
-        float y = 0.f;
-        if (active && s >= 0 && s < len) {
-          const float cur = wave[start + s];
-          y = s > 0 ? cur - kPreemph * wave[start + s - 1] : cur;
-        }
-        yw[2 * m + e] = y * win[n];
-      }
+    for (int m = 0; m < 16; ++m) {
+      const float rot = dpp_mov<0x121>(x1[m]);  // row_ror:1, lane j <- lane j - 1
+      const float prev0 = j == 0 ? (m == 0 ? before : rot_prev) : rot;
+      rot_prev = rot;
+      const int n0 = 2 * (16 * m + j);
+      const int64_t s0 = base + n0;
+      const float y0 = in_clip(s0) ? (s0 > 0 ? x0[m] - kPreemph * prev0 : x0[m]) : 0.f;
+      const float y1 = in_clip(s0 + 1) ? (s0 + 1 > 0 ? x1[m] - kPreemph * x0[m] : x1[m]) : 0.f;
+      yw[2 * m] = y0 * win[n0];
+      yw[2 * m + 1] = y1 * win[n0 + 1];
+    }
   };
   int64_t g0 = (int64_t)blockIdx.x * FPB;
   if (g0 < total) fetch(g0);

@@ -73,9 +73,9 @@ hipError_t launch_layernorm(const LnParams& p, hipStream_t s);
 
 // c = silu((dwconv(g) + b) * aw + ab) along each clip's time axis, zero
 // padding (k - 1) / 2 before and k - 1 - (k - 1) / 2 after; g, c bf16
-// [n][512]; w [512][k].
+// [n][512]; wt: the taps transposed, [k][512].
 hipError_t launch_dwconv(const bf16* g, const int32_t* tok_pos, const int32_t* tok_clip,
-                         const int64_t* token_off, int64_t n, const float* w, int k,
+                         const int64_t* token_off, int64_t n, const float* wt, int k,
                          const float* b, const float* aw, const float* ab, bf16* c,
                          hipStream_t s);
 

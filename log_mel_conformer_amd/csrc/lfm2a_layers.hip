@@ -126,8 +126,11 @@ __global__ void __launch_bounds__(256) k_stem01(const float* __restrict__ feat,
 
 // -------------------------------------------------- depthwise 3x3 stride 2
 // Thread = 8 channels of one output position; 32 threads per position,
-// kPosPerBlock positions per block (the taps stay in registers).
+// kPosPerBlock positions per block (the taps stay in registers). The clip
+// offsets are staged in LDS: a position's clip is a binary search over
+// them, which through global memory is a chain of dependent loads.
 constexpr int kPosPerBlock = 64;
+constexpr int kMaxClipsLds = 512;
 
 __global__ void __launch_bounds__(256) k_dw3s2(const bf16* __restrict__ y,
                                                const int64_t* __restrict__ in_off,
@@ -136,6 +139,13 @@ __global__ void __launch_bounds__(256) k_dw3s2(const bf16* __restrict__ y,
                                                const float* __restrict__ wt,
                                                const float* __restrict__ bias,
                                                bf16* __restrict__ z) {
+  __shared__ int64_t soff[kMaxClipsLds + 1], doff[kMaxClipsLds + 1];
+  const bool lds_off = B <= kMaxClipsLds;
+  if (lds_off)
+    for (int i = threadIdx.x; i <= B; i += 256) {
+      soff[i] = in_off[i];
+      doff[i] = out_off[i];
+    }
   const int c8 = (threadIdx.x & 31) * 8;
   const int w_out = w_in / 2;
   float w[9][8], b[8];
@@ -150,14 +160,17 @@ __global__ void __launch_bounds__(256) k_dw3s2(const bf16* __restrict__ y,
     const float4 a = *(const float4*)(bias + c8), d = *(const float4*)(bias + c8 + 4);
     b[0] = a.x; b[1] = a.y; b[2] = a.z; b[3] = a.w; b[4] = d.x; b[5] = d.y; b[6] = d.z; b[7] = d.w;
   }
+  __syncthreads();
   for (int i = 0; i < kPosPerBlock / 8; ++i) {
     const int64_t pos = (int64_t)blockIdx.x * kPosPerBlock + i * 8 + (threadIdx.x >> 5);
     if (pos >= total_pos) break;
     const int64_t ro = pos / w_out;
     const int fo = (int)(pos - ro * w_out);
-    const int c = find_clip(out_off, B, ro);
-    const int64_t rl = ro - out_off[c];
-    const int64_t hin = in_off[c + 1] - in_off[c];
+    const int64_t* io = lds_off ? soff : in_off;
+    const int64_t* oo = lds_off ? doff : out_off;
+    const int c = find_clip(oo, B, ro);
+    const int64_t rl = ro - oo[c];
+    const int64_t hin = io[c + 1] - io[c];
     float acc[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[e] = b[e];
@@ -165,7 +178,7 @@ __global__ void __launch_bounds__(256) k_dw3s2(const bf16* __restrict__ y,
     for (int dy = 0; dy < 3; ++dy) {
       const int64_t ri = 2 * rl + dy - 1;
       if (ri < 0 || ri >= hin) continue;
-      const bf16* row = y + ((in_off[c] + ri) * w_in) * kStemCh + c8;
+      const bf16* row = y + ((io[c] + ri) * w_in) * kStemCh + c8;
 #pragma unroll
       for (int dz = 0; dz < 3; ++dz) {
         const int fi = 2 * fo + dz - 1;
@@ -183,7 +196,8 @@ __global__ void __launch_bounds__(256) k_dw3s2(const bf16* __restrict__ y,
 }
 
 // ------------------------------------------------------------- LayerNorm
-// One wavefront per 512-wide row, 8 values per lane (two float4), float32
+// A wavefront takes kLnRows 512-wide rows, loads them all (8 values per
+// lane and row, two float4), then normalises them one by one; float32
 // statistics: mean, then the mean square deviation from it.
 __device__ __forceinline__ void ln8(const float* v, const float* w, const float* b, float eps,
                                     int lane, float* y) {
@@ -209,53 +223,68 @@ __device__ __forceinline__ void ln8(const float* v, const float* w, const float*
   }
 }
 
+constexpr int kLnRows = 4;  // rows per wavefront, loaded together
+
 __global__ void __launch_bounds__(256) k_layernorm(LnParams p) {
   const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= p.n) return;
-  float* xr = p.x + row * kD;
-  float v[8], y[8];
+  const int64_t row0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * kLnRows;
+  if (row0 >= p.n) return;
+  float v[kLnRows][8];
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const float4 a = *(const float4*)(xr + h * 256 + lane * 4);
-    v[4 * h] = a.x; v[4 * h + 1] = a.y; v[4 * h + 2] = a.z; v[4 * h + 3] = a.w;
-  }
-  ln8(v, p.w1, p.b1, p.eps, lane, y);
-  if (p.write_x) {
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-      *(float4*)(xr + h * 256 + lane * 4) =
-          make_float4(y[4 * h], y[4 * h + 1], y[4 * h + 2], y[4 * h + 3]);
-  }
-  if (p.w2) {
-    float z[8];
-    ln8(y, p.w2, p.b2, p.eps, lane, z);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) y[i] = z[i];
-  }
-  if (p.a) {
-    bf16* ar = p.a + row * kD;
+  for (int q = 0; q < kLnRows; ++q) {
+    const int64_t row = row0 + q < p.n ? row0 + q : p.n - 1;
+    const float* xr = p.x + row * kD;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const bf16x4 o = {(bf16)y[4 * h], (bf16)y[4 * h + 1], (bf16)y[4 * h + 2],
-                        (bf16)y[4 * h + 3]};
-      *(bf16x4*)(ar + h * 256 + lane * 4) = o;
+      const float4 a = *(const float4*)(xr + h * 256 + lane * 4);
+      v[q][4 * h] = a.x; v[q][4 * h + 1] = a.y; v[q][4 * h + 2] = a.z; v[q][4 * h + 3] = a.w;
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < kLnRows; ++q) {
+    const int64_t row = row0 + q;
+    if (row >= p.n) break;
+    float* xr = p.x + row * kD;
+    float y[8];
+    ln8(v[q], p.w1, p.b1, p.eps, lane, y);
+    if (p.write_x) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        *(float4*)(xr + h * 256 + lane * 4) =
+            make_float4(y[4 * h], y[4 * h + 1], y[4 * h + 2], y[4 * h + 3]);
+    }
+    if (p.w2) {
+      float z[8];
+      ln8(y, p.w2, p.b2, p.eps, lane, z);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) y[i] = z[i];
+    }
+    if (p.a) {
+      bf16* ar = p.a + row * kD;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const bf16x4 o = {(bf16)y[4 * h], (bf16)y[4 * h + 1], (bf16)y[4 * h + 2],
+                          (bf16)y[4 * h + 3]};
+        *(bf16x4*)(ar + h * 256 + lane * 4) = o;
+      }
     }
   }
 }
 
 // ------------------------------------------------ depthwise conv1d + SiLU
-// Thread = 4 channels; 128 threads cover a row, a block two groups of RW
-// consecutive rows. The RW + K - 1 input rows sit in registers; a tap
-// reaching past its own clip's ends (rows of a clip are consecutive) is 0.
-constexpr int kRW = 4;
+// Thread = 4 channels; 128 threads cover a row, a block two groups of kRW
+// consecutive rows. A group loads its kRW + K - 1 input rows into registers
+// up front (one memory latency, not one per row); taps come transposed
+// ([K][512], a float4 per tap), and a tap reaching past its own clip's ends
+// (rows of a clip are consecutive) is 0.
+constexpr int kRW = 16;
 constexpr int kMaxKern = 9;
 
 __global__ void __launch_bounds__(256) k_dwconv(const bf16* __restrict__ g,
                                                 const int32_t* __restrict__ tok_pos,
                                                 const int32_t* __restrict__ tok_clip,
                                                 const int64_t* __restrict__ token_off, int64_t n,
-                                                const float* __restrict__ w, int K,
+                                                const float* __restrict__ wt, int K,
                                                 const float* __restrict__ bias,
                                                 const float* __restrict__ aw,
                                                 const float* __restrict__ ab,
@@ -265,38 +294,49 @@ __global__ void __launch_bounds__(256) k_dwconv(const bf16* __restrict__ g,
   const int64_t r0 = ((int64_t)blockIdx.x * 2 + grp) * kRW;
   if (r0 >= n) return;
   const int lo = (K - 1) / 2;
-  float tw[4][kMaxKern];
+  float tw[kMaxKern][4];
 #pragma unroll
-  for (int e = 0; e < 4; ++e)
-#pragma unroll
-    for (int j = 0; j < kMaxKern; ++j) tw[e][j] = j < K ? w[(ch + e) * K + j] : 0.f;
+  for (int j = 0; j < kMaxKern; ++j) {
+    const float4 v = j < K ? *(const float4*)(wt + (size_t)j * kD + ch) : make_float4(0.f, 0.f, 0.f, 0.f);
+    tw[j][0] = v.x; tw[j][1] = v.y; tw[j][2] = v.z; tw[j][3] = v.w;
+  }
   const float4 bv = *(const float4*)(bias + ch), av = *(const float4*)(aw + ch),
                cv = *(const float4*)(ab + ch);
   const float bb[4] = {bv.x, bv.y, bv.z, bv.w}, aa[4] = {av.x, av.y, av.z, av.w},
               cc[4] = {cv.x, cv.y, cv.z, cv.w};
-  float xin[kRW + kMaxKern - 1][4];
+  // the group's rows: position in the clip and the clip's length, and the
+  // kRW + K - 1 input rows (bf16, two registers a row), all fetched before
+  // the first row is computed
+  int pos_q[kRW], len_q[kRW];
+#pragma unroll
+  for (int q = 0; q < kRW; ++q) {
+    const int64_t r = r0 + q < n ? r0 + q : n - 1;
+    pos_q[q] = tok_pos[r];
+    len_q[q] = tok_clip[r];
+  }
+  bf16x4 raw[kRW + kMaxKern - 1];
 #pragma unroll
   for (int i = 0; i < kRW + kMaxKern - 1; ++i) {
     int64_t rr = r0 - lo + i;
     rr = rr < 0 ? 0 : (rr >= n ? n - 1 : rr);
-    const bf16x4 v = *(const bf16x4*)(g + rr * kD + ch);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) xin[i][e] = (float)v[e];
+    raw[i] = *(const bf16x4*)(g + rr * kD + ch);
   }
+#pragma unroll
+  for (int q = 0; q < kRW; ++q)
+    len_q[q] = (int)(token_off[len_q[q] + 1] - token_off[len_q[q]]);
 #pragma unroll
   for (int q = 0; q < kRW; ++q) {
     const int64_t r = r0 + q;
     if (r >= n) break;
-    const int pos = tok_pos[r];
-    const int c = tok_clip[r];
-    const int len = (int)(token_off[c + 1] - token_off[c]);
+    const int pos = pos_q[q];
+    const int len = len_q[q];
     float acc[4] = {bb[0], bb[1], bb[2], bb[3]};
 #pragma unroll
     for (int j = 0; j < kMaxKern; ++j) {
       const int src = pos + j - lo;
       if (j < K && src >= 0 && src < len) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) acc[e] += tw[e][j] * xin[q + j][e];
+        for (int e = 0; e < 4; ++e) acc[e] += tw[j][e] * (float)raw[q + j][e];
       }
     }
     float o[4];
@@ -386,18 +426,19 @@ hipError_t launch_dw3s2(const bf16* y, const int64_t* in_off, const int64_t* out
 
 hipError_t launch_layernorm(const LnParams& p, hipStream_t s) {
   if (p.n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_layernorm, dim3((unsigned)((p.n + 3) / 4)), dim3(256), 0, s, p);
+  hipLaunchKernelGGL(k_layernorm, dim3((unsigned)((p.n + 4 * kLnRows - 1) / (4 * kLnRows))),
+                     dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
 hipError_t launch_dwconv(const bf16* g, const int32_t* tok_pos, const int32_t* tok_clip,
-                         const int64_t* token_off, int64_t n, const float* w, int k,
+                         const int64_t* token_off, int64_t n, const float* wt, int k,
                          const float* b, const float* aw, const float* ab, bf16* c,
                          hipStream_t s) {
   if (n <= 0) return hipSuccess;
   if (k < 1 || k > kMaxKern) return hipErrorInvalidValue;
   hipLaunchKernelGGL(k_dwconv, dim3((unsigned)((n + 2 * kRW - 1) / (2 * kRW))), dim3(256), 0, s, g,
-                     tok_pos, tok_clip, token_off, n, w, k, b, aw, ab, c);
+                     tok_pos, tok_clip, token_off, n, wt, k, b, aw, ab, c);
   return hipGetLastError();
 }
 
