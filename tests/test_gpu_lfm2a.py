@@ -174,3 +174,41 @@ def test_encode_full_batch_sampled():
         r = rel_l2(got[to[i]:to[i + 1]], want)
         say(f"[gpu]   clip {i}: rel L2 {r:.2e}")
         assert r <= 2e-2, (i, r)
+
+
+def test_encode_beyond_the_page_token_cap():
+    """A 90 s clip (1126 tokens, past the page's kernel cap of 1024) packed
+    with a 2 s clip: two blocks and the adapter against the oracle. The
+    position table is built for the longest clip and the short clip reads
+    its own window of it."""
+    say("[gpu] lfm2a encode: 90 s + 2 s clips (1126 and 26 tokens), two blocks")
+    W = weights(2)
+    lens = [90 * 16000, 32000]
+    clips = clips_of(lens, 90)
+    wave, so = synth.pack(clips)
+    got = lfm2a.encode(model(2), cuda(wave), so).cpu().numpy()
+    to = lfm2a.plan(lens)["token_off"]
+    assert list(np.diff(to)) == [O.num_tokens(n) for n in lens] and to[1] == 1126
+    for i, x in enumerate(clips):
+        want = O.encode(x, W)
+        r = rel_l2(got[to[i]:to[i + 1]], want)
+        say(f"[gpu]   clip {i}: {len(want)} tokens, rel L2 {r:.2e}")
+        assert r <= 2e-2, (i, r)
+
+
+def test_clip_isolation_and_determinism():
+    """A clip's embeddings are the same bits alone and packed between other
+    clips (statistics, stem rows, attention tiles and GEMM rows are all
+    per clip or per row), and a repeated call gives the same bits."""
+    say("[gpu] lfm2a invariant: clip isolation in a pack, determinism")
+    m = model(2)
+    lens = [24321, 320, 40000, 1000]
+    clips = clips_of(lens, 120)
+    wave, so = synth.pack(clips)
+    packed = lfm2a.encode(m, cuda(wave), so).cpu().numpy()
+    again = lfm2a.encode(m, cuda(wave), so).cpu().numpy()
+    assert np.array_equal(packed, again)
+    to = lfm2a.plan(lens)["token_off"]
+    for i, c in enumerate(clips):
+        alone = lfm2a.encode(m, cuda(c), np.array([0, len(c)])).cpu().numpy()
+        assert np.array_equal(alone, packed[to[i]:to[i + 1]]), i
