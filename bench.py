@@ -113,6 +113,37 @@ def copy_probe(torch):
     del src, dst
 
 
+def copy_bandwidth(torch):
+    """Measured device-to-device copy bandwidth (bytes read + written per
+    second, GB/s) of a COPY_PROBE_BYTES copy, best of 6, timed with events
+    after the timed region: a second HBM denominator beside the nominal
+    peak."""
+    src = torch.ones(COPY_PROBE_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    best = None
+    for _ in range(6):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        best = ms if best is None else min(best, ms)
+    del src, dst
+    return 2.0 * COPY_PROBE_BYTES / (best / 1e3) / 1e9
+
+
+def add_copy_denominator(roof, torch):
+    """The measured copy bandwidth, and for an HBM-bound kernel its
+    achieved bandwidth as a fraction of it."""
+    bw = copy_bandwidth(torch)
+    roof["measured_copy_GBps"] = bw
+    if roof.get("bound") == "hbm":
+        roof["frac_of_copy"] = roof["achieved"] / bw
+    return roof
+
+
 def bench_resample(args, torch, ae, synth):
     """32 clips x 30 s of stereo at 48 kHz -> mono 16 kHz (mixdown and the
     Kaiser-sinc resampler, float64 accumulation)."""
@@ -171,6 +202,7 @@ def bench_resample(args, torch, ae, synth):
                       "global_batch": 32, "audio_seconds": audio_s,
                       "output_samples": int(oo[-1]), "parallelism": "none (1 GPU)"},
            "roofline": roof, "cpu_baseline": cpu}
+    add_copy_denominator(rec["roofline"], torch)
     print(json.dumps(rec), flush=True)
 
 
@@ -231,6 +263,7 @@ def bench_merge(args, torch, ae, synth):
                                   "soft-token merge into the embedding rows",
                       "global_batch": 32, "ids": L, "soft_tokens": S, "parallelism": "none (1 GPU)"},
            "roofline": roof, "cpu_baseline": cpu}
+    add_copy_denominator(rec["roofline"], torch)
     print(json.dumps(rec), flush=True)
 
 
@@ -314,6 +347,7 @@ def bench_lfm2a(args, torch, ae, synth):
                       "frames": frames, "audio_seconds": audio_s,
                       "tokens_per_s": tokens / (ms / 1e3), "parallelism": "none (1 GPU)"},
            "roofline": roof, "cpu_baseline": cpu}
+    add_copy_denominator(rec["roofline"], torch)
     print(json.dumps(rec), flush=True)
 
 
@@ -453,6 +487,7 @@ def main():
                       "tokens": tokens, "frames": frames, "audio_seconds": audio_s,
                       "tokens_per_s": tokens / (ms / 1e3), "parallelism": "none (1 GPU)"},
            "roofline": roof, "cpu_baseline": cpu}
+    add_copy_denominator(rec["roofline"], torch)
     print(json.dumps(rec), flush=True)
 
 
