@@ -5,19 +5,30 @@
 // Sixteen lanes per frame, four frames per wavefront. The 512-point real
 // FFT is a 256-point complex FFT of z[n] = x[2n] + i x[2n+1] (the last 96
 // z are zero: the frame is 320 samples), split as 256 = 16 x 16: lane j
-// first takes the 16-point DFT over z[16 m + j] in registers, multiplies by
-// e^{-2 pi i j k / 256}, and the wavefront transposes through LDS; lane j
-// then takes the 16-point DFT over the other index and holds Z[j + 16 k].
-// The real spectrum follows from X[k] = E[k] + e^{-2 pi i k / 512} O[k] with
-// E, O formed from Z[k] and Z[256 - k] (the partner read from LDS). Each
-// 16-point DFT is radix 4 x 4 with constant twiddles. The mel bank has at
-// most two nonzero weights per bin (506 in all), so each band is a short
+// first takes the 16-point DFT over z[16 m + j] in registers (ten nonzero
+// inputs), multiplies by e^{-2 pi i j k / 256}, and the wavefront
+// transposes through LDS; lane j then takes the 16-point DFT over the other
+// index and holds Z[j + 16 k]. The real spectrum follows from
+// 2 X[k] = (Z[k] + conj Z[256-k]) - i e^{-2 pi i k / 512} (Z[k] - conj Z[256-k])
+// (the partner read from LDS); the factor 2 is taken out of the mel
+// weights, which are halved on the host (exact). The mel bank has at most
+// two nonzero weights per bin (506 in all), so each band is a short
 // contiguous dot product over its own bins; lane j takes bands j, j + 16,
-// ..., which spreads narrow and wide bands evenly over the lanes. All
-// exchanges stay inside a wavefront. Window, twiddle and band tables are
+// ..., so the i-th band of every lane comes from the same group of sixteen,
+// and each group reads a fixed number of bins (its widest band's count,
+// the others' weight lists padded with zeros): the loop counts are uniform
+// across the wavefront. All exchanges stay inside a wavefront.
+//
+// Instruction economy (the kernel is VALU-bound): a frame's samples are
+// read through one pointer with immediate offsets (only a clip's first
+// frame, which starts before the clip, takes a checked path), the lane's
+// window weights stay in registers, and the square root and logarithm are
+// the hardware ones (v_sqrt_f32, v_log_f32: about one ulp, far inside the
+// front end's 1e-4 tolerance). Window, twiddle and band tables are
 // computed on the host in double, rounded to float once, and staged in LDS.
 #include <math.h>
 
+#include <algorithm>
 #include <mutex>
 #include <vector>
 
@@ -27,17 +38,18 @@
 namespace ae {
 namespace {
 
-constexpr int kMaxBandW = 640;
+constexpr int kMaxBandW = 1024;
+constexpr int kGroups = kMels / 16;  // band groups: bands 16 i .. 16 i + 15
 constexpr int FPB = 16;        // frames per block (4 per wavefront)
 
 struct MelTables {
   float hann[kFrame];
   float2 tw256[256];        // exp(-2 pi i m / 256)
   float2 tw512[256];        // exp(-2 pi i m / 512), m < 256
-  int band_start[kMels];
-  int band_count[kMels];
-  int band_woff[kMels];
-  float band_w[kMaxBandW];
+  int band_start[kMels];    // first bin a band reads (its padded list stays below bin 257)
+  int group_len[kGroups];   // bins read per band of the group (its widest band's count)
+  int group_woff[kGroups];  // group's weights: [q][16 bands] from here
+  float band_w[kMaxBandW];  // half the filter weights, zero padded
 };
 
 __constant__ MelTables g_mel;
@@ -66,25 +78,46 @@ bool build_tables(MelTables* t) {
   std::vector<double> ff(kMels + 2);
   for (int i = 0; i < kMels + 2; ++i) ff[i] = mel2hz(mels[i]);
   std::vector<double> fk = linspace_d(0.0, kSampleRate / 2, kBins);
-  int woff = 0;
+  // each band's contiguous support and weights
+  std::vector<int> start(kMels, 0), count(kMels, 0);
+  std::vector<std::vector<double>> wts(kMels);
   for (int m = 0; m < kMels; ++m) {
-    int start = -1, count = 0;
+    int st = -1;
     for (int k = 0; k < kBins; ++k) {
       const double down = -(ff[m] - fk[k]) / (ff[m + 1] - ff[m]);
       const double up = (ff[m + 2] - fk[k]) / (ff[m + 2] - ff[m + 1]);
       const double w = fmax(0.0, fmin(down, up));
       if (w > 0.0) {
-        if (start < 0) start = k;
-        if (k != start + count) return false;  // support must be contiguous
-        if (woff + count >= kMaxBandW) return false;
-        t->band_w[woff + count] = (float)w;
-        ++count;
+        if (st < 0) st = k;
+        if (k != st + (int)wts[m].size()) return false;  // support must be contiguous
+        wts[m].push_back(w);
       }
     }
-    t->band_start[m] = start < 0 ? 0 : start;
-    t->band_count[m] = count;
-    t->band_woff[m] = woff;
-    woff += count;
+    start[m] = st < 0 ? 0 : st;
+    count[m] = (int)wts[m].size();
+  }
+  // groups of sixteen bands read a common number of bins; a band whose
+  // padded list would run past the last bin starts earlier, its weights
+  // shifted to the end of the list
+  int woff = 0;
+  for (int i = 0; i < kGroups; ++i) {
+    int q_len = 0;
+    for (int j = 0; j < 16; ++j) q_len = std::max(q_len, count[16 * i + j]);
+    if (woff + 16 * q_len > kMaxBandW) return false;
+    t->group_len[i] = q_len;
+    t->group_woff[i] = woff;
+    for (int j = 0; j < 16; ++j) {
+      const int b = 16 * i + j;
+      const int s0 = std::min(start[b], kBins - q_len);
+      const int shift = start[b] - s0;
+      t->band_start[b] = s0;
+      for (int q = 0; q < q_len; ++q) {
+        const int e = q - shift;
+        t->band_w[woff + 16 * q + j] =
+            (e >= 0 && e < count[b]) ? (float)(0.5 * wts[b][e]) : 0.0f;
+      }
+    }
+    woff += 16 * q_len;
   }
   return true;
 }
@@ -102,6 +135,42 @@ __device__ __forceinline__ int find_clip_lds(const int64_t* off, int B, int64_t 
   return lo;
 }
 
+// 16-point DFT (as dft16) of inputs of which only x[0..9] are nonzero: the
+// first radix-4 stage skips the known zeros.
+__device__ __forceinline__ void dft16_head10(float2 (&x)[16]) {
+#pragma unroll
+  for (int m2 = 0; m2 < 4; ++m2) {
+    // inputs x[m2], x[4 + m2], x[8 + m2] (zero for m2 >= 2), x[12 + m2] = 0
+    const float2 a0 = x[m2], a1 = x[4 + m2];
+    const float2 d13 = mul_mi(a1);
+    float2 s02 = a0, d02 = a0;
+    if (m2 < 2) {
+      s02 = cadd(a0, x[8 + m2]);
+      d02 = csub(a0, x[8 + m2]);
+    }
+    x[m2] = cadd(s02, a1);
+    x[4 + m2] = cadd(d02, d13);
+    x[8 + m2] = csub(s02, a1);
+    x[12 + m2] = csub(d02, d13);
+  }
+#pragma unroll
+  for (int m2 = 1; m2 < 4; ++m2)
+#pragma unroll
+    for (int k1 = 1; k1 < 4; ++k1) x[4 * k1 + m2] = cmul(x[4 * k1 + m2], w16(m2 * k1));
+  float2 y[16];
+#pragma unroll
+  for (int k1 = 0; k1 < 4; ++k1) {
+    float2 a0 = x[4 * k1], a1 = x[4 * k1 + 1], a2 = x[4 * k1 + 2], a3 = x[4 * k1 + 3];
+    dft4(a0, a1, a2, a3);
+    y[k1] = a0;
+    y[k1 + 4] = a1;
+    y[k1 + 8] = a2;
+    y[k1 + 12] = a3;
+  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) x[i] = y[i];
+}
+
 __global__ void __launch_bounds__(256) k_logmel(const float* __restrict__ wave,
                                                 const int64_t* __restrict__ sample_off,
                                                 const int64_t* __restrict__ frame_off, int B,
@@ -109,7 +178,7 @@ __global__ void __launch_bounds__(256) k_logmel(const float* __restrict__ wave,
   __shared__ float2 tw256[256];
   __shared__ float2 tw512[256];
   __shared__ float hann[kFrame];
-  __shared__ int bstart[kMels], bcount[kMels], bwoff[kMels];
+  __shared__ int bstart[kMels];
   __shared__ float bw[kMaxBandW];
   __shared__ int64_t soff[MAXB_LDS + 1], foff[MAXB_LDS + 1];
   // per frame: transpose buffer, then Z in natural order, then magnitudes,
@@ -120,11 +189,7 @@ __global__ void __launch_bounds__(256) k_logmel(const float* __restrict__ wave,
     tw512[i] = g_mel.tw512[i];
   }
   for (int i = threadIdx.x; i < kFrame; i += 256) hann[i] = g_mel.hann[i];
-  for (int i = threadIdx.x; i < kMels; i += 256) {
-    bstart[i] = g_mel.band_start[i];
-    bcount[i] = g_mel.band_count[i];
-    bwoff[i] = g_mel.band_woff[i];
-  }
+  for (int i = threadIdx.x; i < kMels; i += 256) bstart[i] = g_mel.band_start[i];
   for (int i = threadIdx.x; i < kMaxBandW; i += 256) bw[i] = g_mel.band_w[i];
   const bool lds_off = B <= MAXB_LDS;
   if (lds_off)
@@ -139,36 +204,51 @@ __global__ void __launch_bounds__(256) k_logmel(const float* __restrict__ wave,
   const int j = lane & 15;
   float2* T = xbuf[fl];
   float* M = (float*)xbuf[fl];            // magnitudes, after the split
+  // this lane's samples of a frame are 32 m + 2 j + e (m < 10, e < 2): their
+  // window weights, for every frame
+  float wj[20];
+#pragma unroll
+  for (int m = 0; m < 10; ++m)
+#pragma unroll
+    for (int e = 0; e < 2; ++e) wj[2 * m + e] = hann[32 * m + 2 * j + e];
   // Raw samples of the frame group a block handles next: loaded one group
-  // ahead (register double buffer), branch-free: an address outside the
-  // clip is clamped to a valid one and its window weight set to zero.
-  float xr[20], wr[20];
+  // ahead (register double buffer). A frame starts 160 samples early; only
+  // a clip's first frame reaches before the clip, and it (and a slot past
+  // the last frame) takes the checked path, where samples before the clip
+  // are zeros.
+  float xr[20];
   auto fetch = [&](int64_t g0) {
     const int64_t g = g0 + fl;
-    const bool active = g < total;
-    int64_t base = 0, start = 0;
-    if (active) {
+    int64_t base = 0;
+    int lim = 1 << 30;  // samples below this index are zeros (all, past the end)
+    if (g < total) {
       int c;
+      int64_t start;
       if (lds_off) {
         c = find_clip_lds(foff, B, g);
         start = soff[c];
-        base = start + (g - foff[c]) * kHop - kHop;  // frame starts 160 samples early
+        base = start + (g - foff[c]) * kHop - kHop;
       } else {
         c = find_clip(frame_off, B, g);
         start = sample_off[c];
         base = start + (g - frame_off[c]) * kHop - kHop;
       }
+      lim = start > base ? (int)(start - base) : 0;
     }
+    if (lim == 0) {
+      const float* p = wave + base + 2 * j;
 #pragma unroll
-    for (int m = 0; m < 10; ++m) {
-      const int n = 16 * m + j;
+      for (int m = 0; m < 10; ++m)
 #pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const int64_t sidx = base + 2 * n + e;
-        const bool ok = active && sidx >= start;
-        xr[2 * m + e] = wave[ok ? sidx : 0];
-        wr[2 * m + e] = ok ? hann[2 * n + e] : 0.f;
-      }
+        for (int e = 0; e < 2; ++e) xr[2 * m + e] = p[32 * m + e];
+    } else {
+#pragma unroll
+      for (int m = 0; m < 10; ++m)
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int idx = 32 * m + 2 * j + e;
+          xr[2 * m + e] = idx >= lim ? wave[base + idx] : 0.f;
+        }
     }
   };
   int64_t g0 = (int64_t)blockIdx.x * FPB;
@@ -180,11 +260,11 @@ __global__ void __launch_bounds__(256) k_logmel(const float* __restrict__ wave,
     float2 x[16];
 #pragma unroll
     for (int m = 0; m < 16; ++m)
-      x[m] = m < 10 ? make_float2(xr[2 * m] * wr[2 * m], xr[2 * m + 1] * wr[2 * m + 1])
+      x[m] = m < 10 ? make_float2(xr[2 * m] * wj[2 * m], xr[2 * m + 1] * wj[2 * m + 1])
                     : make_float2(0.f, 0.f);
     const int64_t g1 = g0 + (int64_t)gridDim.x * FPB;
     if (g1 < total) fetch(g1);
-    dft16(x);
+    dft16_head10(x);
 #pragma unroll
     for (int k1 = 0; k1 < 16; ++k1) {
       const float2 t = k1 == 0 ? x[0] : cmul(x[k1], tw256[(j * k1) & 255]);
@@ -199,32 +279,35 @@ __global__ void __launch_bounds__(256) k_logmel(const float* __restrict__ wave,
 #pragma unroll
     for (int k2 = 0; k2 < 16; ++k2) T[j + 16 * k2] = x[k2];
     wave_sync();
-    // real split and magnitudes of bins j + 16 k2 (and 256 on lane 0)
+    // real split: twice the magnitudes of bins j + 16 k2 (and 256 on lane 0)
     float mg[16];
 #pragma unroll
     for (int k2 = 0; k2 < 16; ++k2) {
       const int k = j + 16 * k2;
       const float2 zk = x[k2], zn = T[(256 - k) & 255];
-      const float2 E = make_float2(0.5f * (zk.x + zn.x), 0.5f * (zk.y - zn.y));
-      const float2 O = make_float2(0.5f * (zk.y + zn.y), -0.5f * (zk.x - zn.x));
-      const float2 X = cadd(E, cmul(tw512[k], O));
-      mg[k2] = sqrtf(X.x * X.x + X.y * X.y);
+      const float ex = zk.x + zn.x, ey = zk.y - zn.y;  // 2 E[k]
+      const float ox = zk.y + zn.y, oy = zn.x - zk.x;  // 2 O[k]
+      const float2 w = tw512[k];
+      const float xx = fmaf(w.x, ox, fmaf(-w.y, oy, ex));
+      const float xy = fmaf(w.x, oy, fmaf(w.y, ox, ey));
+      mg[k2] = __builtin_amdgcn_sqrtf(fmaf(xx, xx, xy * xy));
     }
-    const float m256 = fabsf(x[0].x - x[0].y);
+    const float m256 = 2.0f * fabsf(x[0].x - x[0].y);
     wave_sync();
 #pragma unroll
     for (int k2 = 0; k2 < 16; ++k2) M[j + 16 * k2] = mg[k2];
     if (j == 0) M[256] = m256;
     wave_sync();
-    // mel bands j, j + 16, ..., then the log
+    // mel bands j, j + 16, ..., then the log (v_log_f32 is log2)
     float out[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int b = j + 16 * i;
-      const int s = bstart[b], cnt = bcount[b], wo = bwoff[b];
+    for (int i = 0; i < kGroups; ++i) {
+      const float* mp = M + bstart[j + 16 * i];
+      const float* wp = bw + g_mel.group_woff[i] + j;
+      const int q_len = g_mel.group_len[i];
       float acc = 0.f;
-      for (int q = 0; q < cnt; ++q) acc += M[s + q] * bw[wo + q];
-      out[i] = logf(acc + kMelFloor);
+      for (int q = 0; q < q_len; ++q) acc = fmaf(mp[q], wp[16 * q], acc);
+      out[i] = __builtin_amdgcn_logf(acc + kMelFloor) * 0.69314718055994530942f;
     }
     wave_sync();
     // the frame's 128 outputs through LDS, then 32 contiguous bytes per lane
