@@ -79,8 +79,12 @@ void timing_end(int cls, hipStream_t s) {
 // ------------------------------------------------------ small kernels
 namespace {
 
+// Host tables ride in the kernel arguments (captured at launch, so the
+// host array may be reused at once and no pinned staging is needed); 256
+// values a launch keeps a 256-clip plan's four tables to five launches.
+constexpr int kI64Chunk = 256;
 struct I64Chunk {
-  int64_t v[64];
+  int64_t v[kI64Chunk];
 };
 
 __global__ void k_write_i64(int64_t* dst, I64Chunk c, int count) {
@@ -198,11 +202,11 @@ hipError_t launch_dequant(const DqJobs& j, hipStream_t s) {
 }
 
 hipError_t launch_write_i64(int64_t* dst, const int64_t* vals, int count, hipStream_t s) {
-  for (int off = 0; off < count; off += 64) {
+  for (int off = 0; off < count; off += kI64Chunk) {
     I64Chunk c;
-    const int k = count - off < 64 ? count - off : 64;
+    const int k = count - off < kI64Chunk ? count - off : kI64Chunk;
     memcpy(c.v, vals + off, sizeof(int64_t) * k);
-    hipLaunchKernelGGL(k_write_i64, dim3(1), dim3(64), 0, s, dst + off, c, k);
+    hipLaunchKernelGGL(k_write_i64, dim3(1), dim3(kI64Chunk), 0, s, dst + off, c, k);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
