@@ -24,6 +24,7 @@ struct ae_model {
   float* R = nullptr;         // [layers][n_dist][hidden]
   float* colscale = nullptr;  // [layers][3 hidden]
   void* conv1r = nullptr;     // [32][9 * 128], model dtype
+  void* conv0f = nullptr;     // bf16 models: conv0's centred taps as matrix-core fragments
   float* dwt = nullptr;       // [layers][conv_kernel][hidden]: light-conv taps transposed
   std::vector<int> attn_nout;  // distinct input clamps among q, k, v (1..3)
   bool q8 = false;             // int8 projections, widened per forward
@@ -434,7 +435,7 @@ ae_status subsample_impl(const ae_model* m, const float* mel, const Plan& pl, co
   if (T == 0) return AE_OK;
   AE_HIP_TRY(launch_token_index(d_tok, B, T, w.tok_pos, w.tok_clip, s));
   AE_LAUNCH(AE_K_CONV0, s, launch_conv0(m->dt, mel, d_frame, d_row, B, pl.rows(), m->w.conv0,
-                                        m->w.ln0, w.y0, s));
+                                        m->conv0f, m->w.ln0, w.y0, s));
   GemmParams p = gemm_params((int)(T * 32), kC1, kC0 * 9, nullptr, 0, m->conv1r, kC0 * 9, w.x1,
                              kC1);
   p.y0 = w.y0;
@@ -816,6 +817,10 @@ static ae_status model_create_impl(const ae_config* cfg, const ae_weights* w, ae
       return fail(e, "qkv scale");
   }
   if ((e = launch_conv1_reorder(dt, w->conv1, m->conv1r, s)) != hipSuccess) return fail(e, "conv1 reorder");
+  if (dt == AE_BF16) {
+    if ((e = hipMalloc(&m->conv0f, kConv0FragBytes)) != hipSuccess) return fail(e, "hipMalloc(conv0)");
+    if ((e = launch_conv0_pack(w->conv0, m->conv0f, s)) != hipSuccess) return fail(e, "conv0 taps");
+  }
   if ((e = hipStreamSynchronize(s)) != hipSuccess) return fail(e, "model tables");
   *out = m;
   return AE_OK;
@@ -840,6 +845,7 @@ void ae_model_destroy(ae_model* m) {
   if (m->R) hipFree(m->R);
   if (m->colscale) hipFree(m->colscale);
   if (m->conv1r) hipFree(m->conv1r);
+  if (m->conv0f) hipFree(m->conv0f);
   if (m->dwt) hipFree(m->dwt);
   delete m;
 }

@@ -71,6 +71,14 @@ __device__ __forceinline__ float dpp_mov(float v) {
 
 // Sum over each quad of lanes (4 consecutive lanes); every lane of the quad
 // gets the same bits.
+// Wave-local LDS hand-off: this wavefront's LDS writes are visible to its
+// own later reads.
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 __device__ __forceinline__ float quad_sum(float v) {
   v += dpp_mov<0xB1>(v);  // quad permutation (1,0,3,2): lane ^ 1
   v += dpp_mov<0x4E>(v);  // quad permutation (2,3,0,1): lane ^ 2

@@ -1,6 +1,5 @@
 // Radix-4 building blocks of the in-register 16-point complex DFTs that
-// the log-mel front ends split their 512-point real FFTs into, and the
-// wavefront-local LDS hand-off between the two DFT passes.
+// the log-mel front ends split their 512-point real FFTs into.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -62,14 +61,6 @@ __device__ __forceinline__ void dft16(float2 (&x)[16]) {
   }
 #pragma unroll
   for (int i = 0; i < 16; ++i) x[i] = y[i];
-}
-
-// Wave-local LDS hand-off: this wavefront's LDS writes are visible to its
-// own later reads.
-__device__ __forceinline__ void wave_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
 }  // namespace ae

@@ -60,9 +60,13 @@ hipError_t launch_logmel(const float* wave, const int64_t* sample_off, const int
                          int B, int64_t total_frames, float* mel, hipStream_t s);
 
 // --------------------------------------------------------------- conv0
+// w0_frag: the bf16 path's matrix-core fragments of the centred taps
+// (launch_conv0_pack, 8 KB); unused for float storage.
 hipError_t launch_conv0(ae_dtype dt, const float* mel, const int64_t* frame_off,
                         const int64_t* row_off, int B, int64_t total_rows, const float* w0,
-                        const float* g0, void* y0, hipStream_t s);
+                        const void* w0_frag, const float* g0, void* y0, hipStream_t s);
+constexpr size_t kConv0FragBytes = 4 * 2 * 64 * 16;
+hipError_t launch_conv0_pack(const float* w0, void* frag, hipStream_t s);
 
 // -------------------------------------------------------------- row norms
 // For each row of h [n][d] (float):

@@ -125,6 +125,29 @@ def test_subsample_ragged_fp32(model1_f32):
     assert off == g.shape[0]
 
 
+def test_subsample_ragged_bf16():
+    """bf16 subsampler (conv0 on the matrix cores with split operands, conv1
+    and in_proj in bf16) on ragged frame counts, including clips shorter
+    than one token window and an empty one."""
+    say("[gpu] subsample: ragged frame counts (1, 2, 3, 5, 99, 2999, 0, 4), bf16")
+    W = weights(1, bf16=True)
+    m = ae.Model(W, dtype="bf16")
+    rng = np.random.default_rng(13)
+    Fs = [1, 2, 3, 5, 99, 2999, 0, 4]
+    mels = [(rng.standard_normal((f, 128)) - 3.0).astype(np.float32) for f in Fs]
+    fo = np.concatenate([[0], np.cumsum(Fs)])
+    g = ae.subsample(m, cuda(np.concatenate(mels)), fo).float().cpu().numpy()
+    off = 0
+    for mm, f in zip(mels, Fs):
+        t = -(-(-(-f // 2)) // 2)
+        if t:
+            r = rel_l2(g[off:off + t], oracle.subsample(mm, W))
+            say(f"    {f} frames: rel {r:.3e}")
+            assert r <= BF16_TOL, (f, r)
+        off += t
+    assert off == g.shape[0]
+
+
 def test_layer_tone_fp32(model1_f32):
     say("[gpu] conformer_layer: 1 layer on the tone clip's tokens, fp32")
     W = weights(1)
