@@ -53,7 +53,7 @@ typedef struct {
 
 /* One Conformer block (the page: GpuConformerBlock). Matrices ("mat") are
  * [out][in] row-major bf16 (y = x W^T); vectors are float32. All device
- * pointers, borrowed: they must outlive the model. */
+ * pointers, 16-byte aligned, borrowed: they must outlive the model. */
 typedef struct {
   const float *ffn_norm_w, *ffn_norm_b;
   const void* ffn_up_w;      const float* ffn_up_b;      /* [n_ff][n_embd] */
@@ -132,7 +132,8 @@ ae_status lfm2a_logmel(const float* wave, const int64_t* sample_off, int32_t B, 
 
 /* --- model ------------------------------------------------------------ */
 
-/* Validate the configuration and build the model's own tables on the
+/* Validate the configuration (every weight pointer non-NULL and 16-byte
+ * aligned, else AE_ERR_INVALID) and build the model's own tables on the
  * current device (bf16 copies of the pointwise stem weights, the
  * projection input columns reordered to the channels-last flatten, the
  * transposed depthwise taps of the stem and of every block's convolution

@@ -307,13 +307,27 @@ __device__ __forceinline__ void epilogue_staged(const GemmParams& p,
 #pragma unroll
               for (int e = 0; e < 4; ++e) o[e] = clampf(acc[i][j][4 * g + e], lo, hi);
               if (p.bias) {
+                const float4 bv = *(const float4*)(p.bias + col);
+                const float bb[4] = {bv.x, bv.y, bv.z, bv.w};
 #pragma unroll
-                for (int e = 0; e < 4; ++e) o[e] = (o[e] + p.bias[col + e]) * p.rscale;
+                for (int e = 0; e < 4; ++e) o[e] = (o[e] + bb[e]) * p.rscale;
               }
             } else if (EPI == EPI_ACT) {
+              // one 16-byte bias load per four columns, and the activation
+              // chosen once per group rather than per value
+              const float4 bv =
+                  p.bias ? *(const float4*)(p.bias + col) : make_float4(0.f, 0.f, 0.f, 0.f);
+              const float bb[4] = {bv.x, bv.y, bv.z, bv.w};
+              if (p.act == ACT_SILU) {
 #pragma unroll
-              for (int e = 0; e < 4; ++e)
-                o[e] = act_apply(p.act, acc[i][j][4 * g + e] + (p.bias ? p.bias[col + e] : 0.0f));
+                for (int e = 0; e < 4; ++e) {
+                  const float y = acc[i][j][4 * g + e] + bb[e];
+                  o[e] = y * sigmoidf_(y);
+                }
+              } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) o[e] = act_apply(p.act, acc[i][j][4 * g + e] + bb[e]);
+              }
             } else {  // EPI_BIAS
               const float4 bv = *(const float4*)(p.bias + col);
               o[0] = acc[i][j][4 * g] + bv.x;

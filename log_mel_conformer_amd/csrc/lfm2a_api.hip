@@ -421,13 +421,18 @@ ae_status lfm2a_model_create(const lfm2a_config* cfg, const lfm2a_weights* w, ae
                      "implemented");
   if (dtype != AE_BF16)
     return set_error(AE_ERR_UNSUPPORTED, "lfm2a_model_create: only AE_BF16 is implemented");
+  // every device pointer non-null and 16-byte aligned (the kernels read
+  // weights and biases with 16-byte loads)
+  auto bad = [](const void* p) { return !p || ((uintptr_t)p & 15) != 0; };
   for (int i = 0; i < 5; ++i)
-    if (!w->stem_w[i] || !w->stem_b[i])
-      return set_error(AE_ERR_INVALID, "lfm2a_model_create: null stem weight");
-  if (!w->pre_encode_out_w || !w->pre_encode_out_b || !w->blocks || !w->adapter_norm_w ||
-      !w->adapter_norm_b || !w->adapter_up_w || !w->adapter_up_b || !w->adapter_down_w ||
-      !w->adapter_down_b)
-    return set_error(AE_ERR_INVALID, "lfm2a_model_create: null weight");
+    if (bad(w->stem_w[i]) || bad(w->stem_b[i]))
+      return set_error(AE_ERR_INVALID, "lfm2a_model_create: stem weight NULL or not 16-byte aligned");
+  if (!w->blocks)
+    return set_error(AE_ERR_INVALID, "lfm2a_model_create: null blocks");
+  if (bad(w->pre_encode_out_w) || bad(w->pre_encode_out_b) || bad(w->adapter_norm_w) ||
+      bad(w->adapter_norm_b) || bad(w->adapter_up_w) || bad(w->adapter_up_b) ||
+      bad(w->adapter_down_w) || bad(w->adapter_down_b))
+    return set_error(AE_ERR_INVALID, "lfm2a_model_create: weight NULL or not 16-byte aligned");
   for (int l = 0; l < cfg->n_layer; ++l) {
     const lfm2a_block_weights& L = w->blocks[l];
     const void* ptrs[] = {L.ffn_norm_w, L.ffn_norm_b, L.ffn_up_w, L.ffn_up_b, L.ffn_down_w,
@@ -439,9 +444,9 @@ ae_status lfm2a_model_create(const lfm2a_config* cfg, const lfm2a_weights* w, ae
                           L.ffn_norm_1_w, L.ffn_norm_1_b, L.ffn_up_1_w, L.ffn_up_1_b,
                           L.ffn_down_1_w, L.ffn_down_1_b, L.ln2_w, L.ln2_b};
     for (const void* p : ptrs)
-      if (!p)
-        return set_error(AE_ERR_INVALID,
-                         "lfm2a_model_create: block " + std::to_string(l) + " has a null weight");
+      if (bad(p))
+        return set_error(AE_ERR_INVALID, "lfm2a_model_create: block " + std::to_string(l) +
+                                             " has a weight NULL or not 16-byte aligned");
   }
   lfm2a_model* m = new lfm2a_model();
   m->cfg = *cfg;

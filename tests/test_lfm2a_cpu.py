@@ -79,6 +79,11 @@ def test_model_create_refuses_before_device_work():
     W = _fake_weights(2)
     W.stem_w[3] = None
     assert _create(cfg, W)[0] == ae.AE_ERR_INVALID
+    # weights and biases are read with 16-byte loads: a misaligned one is refused
+    W = _fake_weights(2)
+    W.blocks[0].ffn_up_b = C.c_void_p(0x10004)
+    st, _ = _create(cfg, W)
+    assert st == ae.AE_ERR_INVALID and b"16-byte" in ae.lib().ae_last_error()
 
 
 def test_calls_refuse_before_device_work():
