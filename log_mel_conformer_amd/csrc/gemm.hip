@@ -99,14 +99,21 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, f32x16 (&acc)[MT][
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int col = col0 / 2 + jp * 32 + g * 8 + h * 4;
+          float ba[4] = {0.f, 0.f, 0.f, 0.f}, bb[4] = {0.f, 0.f, 0.f, 0.f};
+          if (p.bias) {  // 16-byte loads of the a and b halves' biases
+            const float4 va = *(const float4*)(p.bias + col);
+            const float4 vb = *(const float4*)(p.bias + p.glu_d + col);
+            ba[0] = va.x; ba[1] = va.y; ba[2] = va.z; ba[3] = va.w;
+            bb[0] = vb.x; bb[1] = vb.y; bb[2] = vb.z; bb[3] = vb.w;
+          }
           float o[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             float a = clampf(acc[i][2 * jp][4 * g + e], lo, hi);
             float b = clampf(acc[i][2 * jp + 1][4 * g + e], lo, hi);
             if (p.bias) {
-              a += p.bias[col + e];
-              b += p.bias[p.glu_d + col + e];
+              a += ba[e];
+              b += bb[e];
             }
             o[e] = a * sigmoidf_(b);
           }
