@@ -15,6 +15,7 @@
 // slices.
 #include <math.h>
 
+#include <algorithm>
 #include <mutex>
 #include <vector>
 
@@ -25,7 +26,8 @@ namespace ae {
 namespace lfm {
 namespace {
 
-constexpr int kMaxBandW = 768;
+constexpr int kMaxBandW = 1024;
+constexpr int kGroups = kMel / 16;  // band groups: bands 16 i .. 16 i + 15
 constexpr int FPB = 16;        // frames per block (4 per wavefront)
 constexpr int TLD = 17;        // transpose row stride (float2)
 constexpr int MAXB_LDS = 512;  // clips whose offsets are staged in LDS
@@ -34,10 +36,10 @@ struct Tables {
   float win[kNFft];          // periodic Hann of 400 points centred in 512
   float2 tw256[256];         // exp(-2 pi i m / 256)
   float2 tw512[256];         // exp(-2 pi i m / 512), m < 256
-  int band_start[kMel];
-  int band_count[kMel];
-  int band_woff[kMel];
-  float band_w[kMaxBandW];
+  int band_start[kMel];      // first bin a band reads (its padded list stays below bin 257)
+  int group_len[kGroups];    // bins read per band of the group (its widest band's count)
+  int group_woff[kGroups];   // group's weights: [q][16 bands] from here
+  float band_w[kMaxBandW];   // a quarter of the filter weights, zero padded
 };
 
 __constant__ Tables g_tab;
@@ -64,25 +66,47 @@ bool build_tables(Tables* t) {
   const double top = hz_to_mel(8000.0);
   std::vector<double> edge(kMel + 2);
   for (int i = 0; i < kMel + 2; ++i) edge[i] = mel_to_hz(top * i / (kMel + 1));
-  int woff = 0;
+  std::vector<int> start(kMel, 0), count(kMel, 0);
+  std::vector<std::vector<double>> wts(kMel);
   for (int m = 0; m < kMel; ++m) {
     const double lo = edge[m], c = edge[m + 1], hi = edge[m + 2];
-    int start = -1, count = 0;
+    int st = -1;
     for (int k = 0; k < kBins; ++k) {
       const double f = k * 16000.0 / kNFft;
       const double w = fmax(0.0, fmin((f - lo) / (c - lo), (hi - f) / (hi - c))) * 2.0 / (hi - lo);
       if (w > 0.0) {
-        if (start < 0) start = k;
-        if (k != start + count) return false;  // support must be contiguous
-        if (woff + count >= kMaxBandW) return false;
-        t->band_w[woff + count] = (float)w;
-        ++count;
+        if (st < 0) st = k;
+        if (k != st + (int)wts[m].size()) return false;  // support must be contiguous
+        wts[m].push_back(w);
       }
     }
-    t->band_start[m] = start < 0 ? 0 : start;
-    t->band_count[m] = count;
-    t->band_woff[m] = woff;
-    woff += count;
+    start[m] = st < 0 ? 0 : st;
+    count[m] = (int)wts[m].size();
+  }
+  // groups of sixteen bands read a common number of bins; a band whose
+  // padded list would run past the last bin starts earlier, its weights
+  // shifted to the end of the list. The kernel sums four times the power
+  // (twice the spectrum, the split's halves left out), so the weights are
+  // quartered here (exact).
+  int woff = 0;
+  for (int i = 0; i < kGroups; ++i) {
+    int q_len = 0;
+    for (int j = 0; j < 16; ++j) q_len = std::max(q_len, count[16 * i + j]);
+    if (woff + 16 * q_len > kMaxBandW) return false;
+    t->group_len[i] = q_len;
+    t->group_woff[i] = woff;
+    for (int j = 0; j < 16; ++j) {
+      const int b = 16 * i + j;
+      const int s0 = std::min(start[b], kBins - q_len);
+      const int shift = start[b] - s0;
+      t->band_start[b] = s0;
+      for (int q = 0; q < q_len; ++q) {
+        const int e = q - shift;
+        t->band_w[woff + 16 * q + j] =
+            (e >= 0 && e < count[b]) ? (float)(0.25 * wts[b][e]) : 0.0f;
+      }
+    }
+    woff += 16 * q_len;
   }
   return true;
 }
@@ -103,7 +127,7 @@ __global__ void __launch_bounds__(256) k_lfm_logmel(const float* __restrict__ wa
   __shared__ float2 tw256[256];
   __shared__ float2 tw512[256];
   __shared__ float win[kNFft];
-  __shared__ int bstart[kMel], bcount[kMel], bwoff[kMel];
+  __shared__ int bstart[kMel];
   __shared__ float bw[kMaxBandW];
   __shared__ int64_t soff[MAXB_LDS + 1], foff[MAXB_LDS + 1];
   __shared__ __attribute__((aligned(16))) float2 xbuf[FPB][16 * TLD];
@@ -112,11 +136,7 @@ __global__ void __launch_bounds__(256) k_lfm_logmel(const float* __restrict__ wa
     tw512[i] = g_tab.tw512[i];
   }
   for (int i = threadIdx.x; i < kNFft; i += 256) win[i] = g_tab.win[i];
-  for (int i = threadIdx.x; i < kMel; i += 256) {
-    bstart[i] = g_tab.band_start[i];
-    bcount[i] = g_tab.band_count[i];
-    bwoff[i] = g_tab.band_woff[i];
-  }
+  for (int i = threadIdx.x; i < kMel; i += 256) bstart[i] = g_tab.band_start[i];
   for (int i = threadIdx.x; i < kMaxBandW; i += 256) bw[i] = g_tab.band_w[i];
   const bool lds_off = B <= MAXB_LDS;
   if (lds_off)
@@ -138,6 +158,12 @@ __global__ void __launch_bounds__(256) k_lfm_logmel(const float* __restrict__ wa
   // frame's 16 (a DPP rotation within the row; lane 0 takes lane 15's
   // previous m, and for n = 0 loads the sample before the frame itself).
   float yw[32];
+  // this lane's window weights (samples 2 (16 m + j) + e), for every frame
+  float wj[32];
+#pragma unroll
+  for (int m = 0; m < 16; ++m)
+#pragma unroll
+    for (int e = 0; e < 2; ++e) wj[2 * m + e] = win[2 * (16 * m + j) + e];
   auto fetch = [&](int64_t g0) {
     const int64_t g = g0 + fl;
     const bool active = g < total;
@@ -147,6 +173,32 @@ __global__ void __launch_bounds__(256) k_lfm_logmel(const float* __restrict__ wa
       start = lds_off ? soff[c] : sample_off[c];
       len = (lds_off ? soff[c + 1] : sample_off[c + 1]) - start;
       base = (g - (lds_off ? foff[c] : frame_off[c])) * kHop - kCenterPad;
+    }
+    // A frame whose 512 samples and the one before them lie inside the clip
+    // (all but the first two and last two of a clip) reads through one
+    // pointer with immediate offsets and needs no checks. The window is zero
+    // on samples 0..55 and 456..511, so groups m = 0 and 15 are not read;
+    // the one predecessor that would come from them (lane 0, m = 1) meets
+    // a zero window as well.
+    if (active && base >= 1 && base + kNFft <= len) {
+      const float* p = wave + start + base + 2 * j;
+      float x0[16], x1[16];
+      x0[0] = x1[0] = x0[15] = x1[15] = 0.f;
+#pragma unroll
+      for (int m = 1; m < 15; ++m) {
+        x0[m] = p[32 * m];
+        x1[m] = p[32 * m + 1];
+      }
+      float rot_prev = 0.f;
+#pragma unroll
+      for (int m = 0; m < 16; ++m) {
+        const float rot = dpp_mov<0x121>(x1[m]);  // row_ror:1, lane j <- lane j - 1
+        const float prev0 = j == 0 ? rot_prev : rot;
+        rot_prev = rot;
+        yw[2 * m] = (x0[m] - kPreemph * prev0) * wj[2 * m];
+        yw[2 * m + 1] = (x1[m] - kPreemph * x0[m]) * wj[2 * m + 1];
+      }
+      return;
     }
     auto in_clip = [&](int64_t s) { return active && s >= 0 && s < len; };
     float x0[16], x1[16];
@@ -167,8 +219,8 @@ __global__ void __launch_bounds__(256) k_lfm_logmel(const float* __restrict__ wa
       const int64_t s0 = base + n0;
       const float y0 = in_clip(s0) ? (s0 > 0 ? x0[m] - kPreemph * prev0 : x0[m]) : 0.f;
       const float y1 = in_clip(s0 + 1) ? (s0 + 1 > 0 ? x1[m] - kPreemph * x0[m] : x1[m]) : 0.f;
-      yw[2 * m] = y0 * win[n0];
-      yw[2 * m + 1] = y1 * win[n0 + 1];
+      yw[2 * m] = y0 * wj[2 * m];
+      yw[2 * m + 1] = y1 * wj[2 * m + 1];
     }
   };
   int64_t g0 = (int64_t)blockIdx.x * FPB;
@@ -197,18 +249,20 @@ __global__ void __launch_bounds__(256) k_lfm_logmel(const float* __restrict__ wa
 #pragma unroll
     for (int k2 = 0; k2 < 16; ++k2) T[j + 16 * k2] = x[k2];
     wave_sync();
-    // real split and powers of bins j + 16 k2 (and 256 on lane 0)
+    // real split: four times the powers of bins j + 16 k2 (and 256 on lane 0)
     float pw[16];
 #pragma unroll
     for (int k2 = 0; k2 < 16; ++k2) {
       const int k = j + 16 * k2;
       const float2 zk = x[k2], zn = T[(256 - k) & 255];
-      const float2 E = make_float2(0.5f * (zk.x + zn.x), 0.5f * (zk.y - zn.y));
-      const float2 O = make_float2(0.5f * (zk.y + zn.y), -0.5f * (zk.x - zn.x));
-      const float2 X = cadd(E, cmul(tw512[k], O));
-      pw[k2] = X.x * X.x + X.y * X.y;
+      const float ex = zk.x + zn.x, ey = zk.y - zn.y;  // 2 E[k]
+      const float ox = zk.y + zn.y, oy = zn.x - zk.x;  // 2 O[k]
+      const float2 w = tw512[k];
+      const float xx = fmaf(w.x, ox, fmaf(-w.y, oy, ex));
+      const float xy = fmaf(w.x, oy, fmaf(w.y, ox, ey));
+      pw[k2] = fmaf(xx, xx, xy * xy);
     }
-    const float nyq = x[0].x - x[0].y;
+    const float nyq = 2.0f * (x[0].x - x[0].y);
     const float p256 = nyq * nyq;
     wave_sync();
 #pragma unroll
@@ -216,14 +270,16 @@ __global__ void __launch_bounds__(256) k_lfm_logmel(const float* __restrict__ wa
     if (j == 0) M[256] = p256;
     wave_sync();
     // mel bands j, j + 16, ..., then the log
+    // (uniform trip counts per group of sixteen bands; v_log_f32 is log2)
     float out[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int b = j + 16 * i;
-      const int s = bstart[b], cnt = bcount[b], wo = bwoff[b];
+    for (int i = 0; i < kGroups; ++i) {
+      const float* mp = M + bstart[j + 16 * i];
+      const float* wp = bw + g_tab.group_woff[i] + j;
+      const int q_len = g_tab.group_len[i];
       float acc = 0.f;
-      for (int q = 0; q < cnt; ++q) acc += M[s + q] * bw[wo + q];
-      out[i] = logf(acc + kLogEps);
+      for (int q = 0; q < q_len; ++q) acc = fmaf(mp[q], wp[16 * q], acc);
+      out[i] = __builtin_amdgcn_logf(acc + kLogEps) * 0.69314718055994530942f;
     }
     wave_sync();
     float* O = M + 260;
