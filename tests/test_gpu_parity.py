@@ -174,6 +174,31 @@ def test_layer_packed_positions_fp32(model1_f32):
     assert rel_l2(g[:7], want[:7]) <= FP32_TOL and rel_l2(g[7:], want[7:]) <= FP32_TOL
 
 
+def test_layer_packed_positions_bf16():
+    """One bf16 layer (bf16 GEMMs and epilogues, the packed-bf16 dot
+    products of the attention logits, bf16 light conv) on three packed
+    clips of 1, 11 and 300 tokens: a clip shorter than the window, one
+    that just fills it, and a long one; each against the oracle with the
+    same bf16-rounded weights."""
+    say("[gpu] conformer_layer: packed clips of 1, 11 and 300 tokens, bf16")
+    W = weights(1, bf16=True)
+    m = ae.Model(W, dtype="bf16")
+    rng = np.random.default_rng(14)
+    lens = [1, 11, 300]
+    h0 = rng.standard_normal((sum(lens), 1024)).astype(np.float32)
+    pos = np.concatenate([np.arange(n) for n in lens]).astype(np.int32)
+    h = cuda(h0)
+    ae.conformer_layer(m, 0, h, cuda(pos, torch.int32))
+    g = h.cpu().numpy()
+    off = 0
+    for n in lens:
+        want = oracle.conformer_layer(h0[off:off + n], W["layers"][0], np.arange(n, dtype=np.int32))
+        r = rel_l2(g[off:off + n], want)
+        say(f"    {n} tokens: rel {r:.3e}")
+        assert r <= BF16_TOL, (n, r)
+        off += n
+
+
 def test_layer_clamps_and_softcap_bind_fp32():
     """Bounds of +-0.5 make every clamp bind; large q weights and
     per_dim_scale above 20 (softplus pass-through) push logits past the
