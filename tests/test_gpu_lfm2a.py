@@ -75,6 +75,37 @@ def test_logmel_ragged_batch():
         assert r <= 1e-4, (i, r, float(np.abs(g - want).max()))
 
 
+def test_more_clips_than_the_lds_offset_tables():
+    """700 short clips: past the 512 whose offsets the front end and the
+    stem's depthwise kernel stage in LDS. Every clip's features against the
+    oracle, then the encoder (one block) on a sample of the clips."""
+    say("[gpu] lfm2a: 700 ragged short clips, logmel of all, encoder (1 block) on 5")
+    rng = np.random.default_rng(22)
+    lens = rng.integers(320, 4000, 700)
+    lens[[5, 600]] = [0, 320]
+    clips = clips_of([int(n) for n in lens], 3000)
+    wave, so = synth.pack(clips)
+    wd = cuda(wave)
+    got = lfm2a.logmel(wd, so).cpu().numpy()
+    fo = lfm2a.plan([len(c) for c in clips])["frame_off"]
+    for i, x in enumerate(clips):
+        if len(x) == 0:
+            continue
+        r = rel_l2(got[fo[i]:fo[i + 1]], O.log_mel(x))
+        # a clip of 320..479 samples has two statistics frames, which share
+        # most of their samples: bins that barely differ between them have a
+        # std near zero, and the normalisation scales the float32 spectrum's
+        # rounding by 1 / (std + 1e-5) (measured up to 2.6e-4 here)
+        bar = 1e-4 if len(x) // 160 >= 3 else 1e-3
+        assert r <= bar, (i, len(x), r)
+    W = weights(1)
+    out = lfm2a.encode(model(1), wd, so).cpu().numpy()
+    to = lfm2a.plan([len(c) for c in clips])["token_off"]
+    for i in (0, 1, 600, 650, 699):
+        r = rel_l2(out[to[i]:to[i + 1]], O.encode(clips[i], W))
+        assert r <= 2e-2, (i, r)
+
+
 def test_attention_kernel_ragged():
     say("[gpu] lfm2a xl_attention alone: 10 clips of 1..376 tokens, t_max 400")
     rng = np.random.default_rng(5)

@@ -68,6 +68,38 @@ def test_logmel_ragged_batch_and_edges():
         off += f
 
 
+def test_more_clips_than_the_lds_offset_tables():
+    """700 short clips: past the 512 clips whose offsets the kernels stage in
+    LDS, so the clip lookups go through global memory. The log-mel of every
+    seventh clip and of those around index 512 against the oracle, then the
+    encoder (one layer and the head, bf16) on a sample of the clips."""
+    say("[gpu] 700 ragged short clips: log-mel of 106, encoder (1 layer, bf16) on 6")
+    rng = np.random.default_rng(21)
+    lens = rng.integers(0, 3000, 700)
+    lens[[3, 400, 699]] = [0, 160, 161]
+    clips = [synth.white_clip(1000 + i, int(n)) if n else np.zeros(0, np.float32)
+             for i, n in enumerate(lens)]
+    wave, so = synth.pack(clips)
+    wd = cuda(wave)
+    g = ae.logmel(wd, so).cpu().numpy()
+    F = [oracle.num_frames(len(c)) for c in clips]
+    assert g.shape[0] == sum(F)
+    fo = np.concatenate([[0], np.cumsum(F)])
+    for i in sorted(set(range(0, 700, 7)) | {3, 400, 511, 512, 513, 699}):
+        if F[i]:
+            logmel_ok(g[fo[i]:fo[i + 1]], oracle.log_mel(clips[i]))
+    W = weights(1, bf16=True)
+    m = ae.Model(W, dtype="bf16")
+    out = ae.encode(m, wd, so).cpu().numpy()
+    T = [oracle.num_tokens(len(c)) for c in clips]
+    to = np.concatenate([[0], np.cumsum(T)])
+    assert out.shape[0] == to[-1]
+    for i in (0, 1, 401, 650, 698, 699):
+        if T[i]:
+            r = rel_l2(out[to[i]:to[i + 1]], oracle.encode_clips([clips[i]], W)[0])
+            assert r <= BF16_TOL, (i, r)
+
+
 def test_logmel_silence_and_impulse():
     say("[gpu] logmel: silence and impulse")
     z = np.zeros(16000, np.float32)
