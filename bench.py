@@ -364,7 +364,7 @@ def main():
     ap.add_argument("--copy-probe", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for {args.gpus}); "
+        print(f"bench.py: runs on one GPU only (asked for {args.gpus}); "
               "clips are independent, so more GPUs would each encode their own share.",
               file=sys.stderr)
         sys.exit(2)

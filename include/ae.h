@@ -40,7 +40,7 @@ typedef enum {
   AE_ERR_INVALID = 1,     /* null pointer, negative size, bad layer index */
   AE_ERR_SHAPE = 2,       /* a weight or size does not fit the configuration */
   AE_ERR_CAPACITY = 3,    /* workspace too small, or an index beyond int32 */
-  AE_ERR_UNSUPPORTED = 4, /* a configuration this build does not implement */
+  AE_ERR_UNSUPPORTED = 4, /* a configuration the library does not implement */
   AE_ERR_HIP = 5          /* a HIP runtime call failed */
 } ae_status;
 

@@ -716,7 +716,7 @@ static ae_status model_create_impl(const ae_config* cfg, const ae_weights* w, ae
     return set_error(AE_ERR_UNSUPPORTED, "attention_context_right " + std::to_string(c.ctx_right) +
                                              " is not supported (only 0)");
   if (c.hidden != 1024 || c.heads <= 0 || c.hidden % c.heads != 0 || c.hidden / c.heads != 128)
-    return set_error(AE_ERR_UNSUPPORTED, "this build implements hidden 1024 with 128-wide heads");
+    return set_error(AE_ERR_UNSUPPORTED, "only hidden 1024 with 128-wide heads is implemented");
   if (c.layers < 1 || c.layers > 256) return set_error(AE_ERR_INVALID, "layers must be in 1..256");
   if (c.ff < 128 || c.ff % 128 != 0) return set_error(AE_ERR_UNSUPPORTED, "ff must be a multiple of 128");
   if (c.conv_kernel < 1 || c.conv_kernel > 16)
