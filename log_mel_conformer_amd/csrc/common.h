@@ -51,8 +51,11 @@ template <typename T> __device__ __forceinline__ T from_f32(float x);
 template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
 template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }
 
+// Clamp to [lo, hi] as one v_med3_f32: the median of x, lo and hi is the
+// clamped value whenever lo <= hi, which every caller guarantees (the model
+// checks its clip bounds at creation; unclamped paths pass -inf and inf).
 __device__ __forceinline__ float clampf(float x, float lo, float hi) {
-  return fminf(fmaxf(x, lo), hi);
+  return __builtin_amdgcn_fmed3f(x, lo, hi);
 }
 // 1 / (1 + e^-x) with the hardware reciprocal (about 1 ulp) rather than an
 // IEEE divide, which costs ten instructions; exp overflow gives 0 and 1 at

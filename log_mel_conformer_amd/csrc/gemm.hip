@@ -219,6 +219,16 @@ template <typename TS> __device__ __forceinline__ void get4s(const unsigned char
   }
 }
 
+// LDS bytes of one 32-row slab per wavefront row in the staged epilogue
+// (none for the direct SiLU and GLU epilogues); a kernel whose stage ring
+// is smaller than that gets the larger LDS array.
+template <typename TO, int EPI, int BN, int WM>
+constexpr int staged_slab_bytes() {
+  constexpr int es = EPI == EPI_RESID ? 4 : (int)sizeof(TO);
+  constexpr int outn = EPI == EPI_GLU ? BN / 2 : BN;
+  return (EPI == EPI_SILU || EPI == EPI_GLU) ? 0 : WM * 32 * (outn * es + 4 * es);
+}
+
 constexpr int staged_slabs(int mt, int slab, int ldsb) {
   int best = 1;
   for (int s = 1; s <= mt; ++s)
@@ -576,8 +586,16 @@ __device__ __forceinline__ int swz_rb(int row, int c) {
 // each wavefront waits only for its own loads of the stage it is about to
 // read (exact vmcnt), then a bare barrier publishes the stage. Rows past M
 // read row M - 1 (their results are never stored).
+//
+// FB is the number of register sets for the MFMA fragments. With two, the
+// reads of the next substep are in flight under the MFMAs of the current
+// one; with one, each substep reads its fragments and then multiplies,
+// which saves (MT + NTL) * 4 registers a lane. That fits a 192x256 tile's
+// four wavefronts in 256 registers (accumulators included), so with a
+// two-stage ring two blocks share a CU and each SIMD runs two wavefronts
+// that hide each other's waits.
 template <typename T, typename TO, int BM, int BN, int WM, int WN, int RB, int STAGES, int EPI,
-          int OCC, int GM>
+          int OCC, int GM, int FB>
 __global__ void __launch_bounds__(WM * WN * 64, OCC) k_gemm_dl(GemmParams p) {
   constexpr int NW = WM * WN;
   constexpr int EPC = 16 / sizeof(T);
@@ -593,8 +611,11 @@ __global__ void __launch_bounds__(WM * WN * 64, OCC) k_gemm_dl(GemmParams p) {
   static_assert(GROUPS % NW == 0, "groups spread evenly over wavefronts");
   constexpr int GPW = GROUPS / NW;             // loads per wavefront per stage
   static_assert(GPW * (STAGES - 2) < 64, "vmcnt range");
+  static_assert(FB == 1 || FB == 2, "one or two fragment sets");
   constexpr int STAGE = (BM + BN) * RB;
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[STAGES * STAGE];
+  constexpr int SLAB0 = staged_slab_bytes<TO, EPI, BN, WM>();
+  constexpr int SMEM = STAGES * STAGE > SLAB0 ? STAGES * STAGE : SLAB0;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[SMEM];
 
   const int tid = threadIdx.x, lane = tid & 63;
   // wavefront index as a scalar: LDS destinations (m0) then need no
@@ -654,12 +675,12 @@ __global__ void __launch_bounds__(WM * WN * 64, OCC) k_gemm_dl(GemmParams p) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-  // Fragments are double-buffered in registers: the reads of substep
-  // st + 1 (or of the next stage's substep 0) are issued before the MFMAs
-  // of substep st, and sched_barrier keeps the scheduler from sinking them
-  // back next to their use.
+  // With FB == 2, fragments are double-buffered in registers: the reads of
+  // substep st + 1 (or of the next stage's substep 0) are issued before the
+  // MFMAs of substep st, and sched_barrier keeps the scheduler from sinking
+  // them back next to their use.
   constexpr int NSUB = CPR / 2;
-  u32x4 fa[2][MT], fb[2][NTL];
+  u32x4 fa[FB][MT], fb[FB][NTL];
   auto load_frags = [&](int sel, const unsigned char* sb, int st) {
     const int c = 2 * st + (lane >> 5);
 #pragma unroll
@@ -679,7 +700,7 @@ __global__ void __launch_bounds__(WM * WN * 64, OCC) k_gemm_dl(GemmParams p) {
   else wait_vmcnt<0>();
   bare_barrier();
   if (STAGES - 1 < nk) issue(STAGES - 1, STAGES - 1);
-  load_frags(0, smem, 0);
+  if constexpr (FB == 2) load_frags(0, smem, 0);
 
   // One substep: the MFMAs on fragment set `cur`, with the operations the
   // caller emitted just before threaded between them: after each of the
@@ -711,6 +732,34 @@ __global__ void __launch_bounds__(WM * WN * 64, OCC) k_gemm_dl(GemmParams p) {
   };
   // Every iteration but the last publishes the next stage before its last
   // substep; the last iteration is peeled so the loop body has no branch.
+  if constexpr (FB == 1) {
+    for (int kt = 0; kt + 1 < nk; ++kt) {
+      const unsigned char* sb = smem + (kt % STAGES) * STAGE;
+#pragma unroll
+      for (int st = 0; st < NSUB; ++st) {
+        load_frags(0, sb, st);
+        if (st + 1 < NSUB) {
+          mfmas(0, 0, 0);
+          continue;
+        }
+        // the last substep's fragments have landed: publish stage kt + 1
+        // and refill stage kt's buffer (the same rules as below), with the
+        // loads threaded between this substep's MFMAs
+        wait_lgkmcnt0();
+        if (kt + STAGES - 1 < nk) wait_vmcnt<GPW * (STAGES - 2)>();
+        else wait_vmcnt<0>();
+        bare_barrier();
+        issue(kt % STAGES, min(kt + STAGES, nk - 1));
+        mfmas(0, 0, GPW);
+      }
+    }
+    const unsigned char* sb = smem + ((nk - 1) % STAGES) * STAGE;
+#pragma unroll
+    for (int st = 0; st < NSUB; ++st) {
+      load_frags(0, sb, st);
+      mfmas(0, 0, 0);
+    }
+  } else {
   for (int kt = 0; kt + 1 < nk; ++kt) {
     const unsigned char* sb = smem + (kt % STAGES) * STAGE;
 #pragma unroll
@@ -748,22 +797,23 @@ __global__ void __launch_bounds__(WM * WN * 64, OCC) k_gemm_dl(GemmParams p) {
       mfmas(cur, st + 1 < NSUB ? NLOAD : 0, 0);
     }
   }
+  }
   // Staging wins where the epilogue is light (plain store, residual add,
   // bias); SiLU and GLU spend enough arithmetic per value that storing
   // straight from registers, overlapped with that arithmetic, is faster.
   if constexpr (EPI == EPI_SILU || EPI == EPI_GLU)
     epilogue<TO, MT, NTL, EPI>(p, acc, m0 + wm * WTM, n0 + wn * WTN, seg, lane);
   else
-    epilogue_staged<TO, BM, BN, WM, WN, EPI, STAGES * STAGE>(p, acc, smem, m0, n0, wm, wn, seg,
+    epilogue_staged<TO, BM, BN, WM, WN, EPI, SMEM>(p, acc, smem, m0, n0, wm, wn, seg,
                                                             wave, lane);
 }
 
 template <typename T, typename TO, int BM, int BN, int WM, int WN, int RB, int STAGES, int EPI,
-          int OCC = 1, int GM = 4>
+          int OCC = 1, int GM = 4, int FB = 2>
 hipError_t run_dl(const GemmParams& p, hipStream_t s) {
   if (p.M <= 0) return hipSuccess;
   const int tiles = ((p.M + BM - 1) / BM) * (p.N / BN);
-  hipLaunchKernelGGL((k_gemm_dl<T, TO, BM, BN, WM, WN, RB, STAGES, EPI, OCC, GM>), dim3(tiles),
+  hipLaunchKernelGGL((k_gemm_dl<T, TO, BM, BN, WM, WN, RB, STAGES, EPI, OCC, GM, FB>), dim3(tiles),
                      dim3(WM * WN * 64), 0, s, p);
   return hipGetLastError();
 }
@@ -795,7 +845,8 @@ hipError_t dispatch_f32(int epi, int aload, const GemmParams& p, hipStream_t s) 
 // the row count, the output width (tiles per wave of 256 CUs) and the depth
 // of K.
 //  wide   (N % 256 == 0, N >= 2048): 256x256, 8 wavefronts of 128x64, two 128-byte stages
-//  deep   (K >= 2048, N % 256 == 0): 192x256, 4 wavefronts of 96x128
+//  paired (other N % 256 == 0, no residual add): 192x256, 4 wavefronts of 96x128 with one
+//         fragment set, two 64-byte stages, two blocks per CU
 //  narrow (otherwise):               256x128, 8 wavefronts of 64x64, two blocks per CU
 template <int EPI, typename TO>
 hipError_t run_bf16(const GemmParams& p, hipStream_t s) {
@@ -809,12 +860,16 @@ hipError_t run_bf16(const GemmParams& p, hipStream_t s) {
     return run_dl<bf16, TO, 128, 128, 2, 2, 64, 3, EPI, 3, 4>(p, s);
   }
   // measured inside the encoder (24000 rows): 256x256 tiles in bands of 4
-  // row tiles for the wide projections, 192x256 with two blocks per CU for
-  // the deep one, two 256x128 blocks per CU for the square ones
+  // row tiles for the wide projections; paired 192x256 blocks for FFN W2
+  // (208 -> 184 us against one 192x256 block per CU with double-buffered
+  // fragments and three stages), the attention post projection (67 -> 58)
+  // and the head's projections (85 -> 75 on average); the fp32 residual
+  // add of linear_end measured 100 -> 103 that way, the wide ones 1-5%
+  // slower, so they keep their shapes
   if (p.N % 256 == 0 && p.N >= 2048)
     return run_dl<bf16, TO, 256, 256, 2, 4, 128, 2, EPI, 1, 4>(p, s);
-  if (p.K >= 2048 && p.N % 256 == 0)
-    return run_dl<bf16, TO, 192, 256, 2, 2, 64, 3, EPI, 2, 4>(p, s);
+  if (p.N % 256 == 0 && EPI != EPI_RESID)
+    return run_dl<bf16, TO, 192, 256, 2, 2, 64, 2, EPI, 2, 4, 1>(p, s);
   return run_dl<bf16, TO, 256, 128, 4, 2, 64, 3, EPI, 2, 2>(p, s);
 }
 
