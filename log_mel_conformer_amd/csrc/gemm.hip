@@ -543,6 +543,24 @@ __device__ __forceinline__ void tile_of(int b, int nblk, int tiles_m, int tiles_
   tm = m_lo + (r - tn * gm);
 }
 
+// Buffer loads straight to LDS (buffer_load_dwordx4 ... lds): the LLVM
+// intrinsic, declared by name, with the 128-bit buffer resource as four
+// dwords: base address (48 bits, stride 0), size in bytes (reads at or past
+// it return zeros) and the gfx9 format word.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+__device__ void raw_buffer_load_lds(i32x4 rsrc, __attribute__((address_space(3))) void* lds,
+                                    int size, uint32_t voffset, uint32_t soffset, int offset,
+                                    int aux) __asm("llvm.amdgcn.raw.buffer.load.lds");
+__device__ __forceinline__ i32x4 buffer_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)base;
+  i32x4 r;
+  r.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  r.y = __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32) & 0xFFFF);
+  r.z = __builtin_amdgcn_readfirstlane((int)bytes);
+  r.w = 0x00020000;
+  return r;
+}
+
 // s_waitcnt vmcnt(N) with every other counter left alone (gfx9 encoding:
 // vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
 template <int N>
@@ -578,14 +596,14 @@ __device__ __forceinline__ int swz_rb(int row, int c) {
 
 // Plain-operand GEMM with direct global->LDS loads and a STAGES-deep ring
 // of LDS stages (each BM + BN rows of RB bytes, i.e. RB / sizeof(T) of k).
-// Every 1-KB group of rows is filled by one global_load_lds_dwordx4 of one
-// wavefront, lane l landing at byte 16 l of the group; the XOR swizzle is
+// Every 1-KB group of rows is filled by one buffer_load_dwordx4 ... lds of
+// one wavefront, lane l landing at byte 16 l of the group; the XOR swizzle is
 // applied on the source side (lane l fetches the logical chunk that belongs
 // at its physical slot), so the LDS image is the swizzled layout the
 // fragment reads expect. Loads run STAGES - 1 stages ahead of the MFMAs;
 // each wavefront waits only for its own loads of the stage it is about to
 // read (exact vmcnt), then a bare barrier publishes the stage. Rows past M
-// read row M - 1 (their results are never stored).
+// read zeros (their results are never stored).
 //
 // FB is the number of register sets for the MFMA fragments. With two, the
 // reads of the next substep are in flight under the MFMAs of the current
@@ -635,35 +653,55 @@ __global__ void __launch_bounds__(WM * WN * 64, OCC) k_gemm_dl(GemmParams p) {
   const T* Ab = (const T*)p.A[seg];
   const T* Bb = (const T*)p.Bm[seg];
 
-  const T* src[GPW];
+  // Loads are buffer loads straight to LDS with a buffer resource per
+  // operand: A based at the tile's first row and sized to the rows below M,
+  // B at the weight matrix. The range check covers only the per-lane
+  // offset, so an A group's row offset is folded into it (one register per
+  // group) and A rows past M read zeros (their results are never stored);
+  // B groups share one per-lane offset and keep their row offset in a
+  // scalar register. The k advance is a scalar offset.
+  static_assert(NW % 2 == 0, "groups of one wavefront share the swizzle parity");
+  const int l = lane / CPR, pc = lane % CPR;
+  // the swizzle of row g * RPG + l: with 128-byte rows it depends on g's
+  // parity, which equals the wavefront's (NW is even)
+  const int sw = RB == 128 ? (((wave & 1) * 4 + (l >> 1)) & 7) : ((l >> 2) & 3);
+  const int c = pc ^ sw;
+  const uint32_t lane_a = (uint32_t)((l * p.lda + c * EPC) * (int)sizeof(T));
+  const uint32_t lane_b = (uint32_t)((l * p.ldb + c * EPC) * (int)sizeof(T));
+  const size_t a_bytes = (size_t)(p.M - m0) * p.lda * sizeof(T);
+  const i32x4 rs_a = buffer_rsrc(Ab + (size_t)m0 * p.lda,
+                                 (uint32_t)(a_bytes < 0xFFFFFFFFull ? a_bytes : 0xFFFFFFFFull));
+  const i32x4 rs_b = buffer_rsrc(Bb, 0xFFFFFFFFu);
+  uint32_t voff[GPW], soff[GPW];
 #pragma unroll
   for (int i = 0; i < GPW; ++i) {
-    const int g = wave + i * NW;
-    const int r = g * RPG + lane / CPR;
-    const int pc = lane % CPR;
-    const int c = RB == 128 ? (pc ^ ((r >> 1) & 7)) : (pc ^ ((r >> 2) & 3));
-    if (r < BM) {
-      const int gm = min(m0 + r, p.M - 1);
-      src[i] = Ab + (size_t)gm * p.lda + c * EPC;
+    const int r0 = (wave + i * NW) * RPG;
+    if (r0 < BM) {
+      voff[i] = lane_a + (uint32_t)(r0 * p.lda * (int)sizeof(T));
+      soff[i] = 0;
     } else {
-      const int br = r - BM;
-      int wrow;
+      const int br0 = r0 - BM;
+      int wrow0;
       if (EPI == EPI_GLU) {
-        const int vr = n0 + br;
-        wrow = ((vr >> 5) & 1) * p.glu_d + (vr >> 6) * 32 + (vr & 31);
+        // 32 'a' rows, then 32 'b' rows: a group's rows stay in one run
+        const int vr = n0 + br0;
+        wrow0 = ((vr >> 5) & 1) * p.glu_d + (vr >> 6) * 32 + (vr & 31);
       } else {
-        wrow = nloc + br;
+        wrow0 = nloc + br0;
       }
-      src[i] = Bb + (size_t)wrow * p.ldb + c * EPC;
+      voff[i] = lane_b;
+      // uniform by construction; say so, or the compiler may keep it in a
+      // vector register and loop over its distinct values
+      soff[i] = __builtin_amdgcn_readfirstlane((uint32_t)((size_t)wrow0 * p.ldb * sizeof(T)));
     }
   }
   auto issue = [&](int buf, int kt) {
 #pragma unroll
     for (int i = 0; i < GPW; ++i) {
       const int g = wave + i * NW;
-      __builtin_amdgcn_global_load_lds(
-          (const __attribute__((address_space(1))) void*)(src[i] + (size_t)kt * BK),
-          (__attribute__((address_space(3))) void*)(smem + buf * STAGE + g * 1024), 16, 0, 0);
+      raw_buffer_load_lds(g * RPG < BM ? rs_a : rs_b,
+                          (__attribute__((address_space(3))) void*)(smem + buf * STAGE + g * 1024),
+                          16, voff[i], soff[i] + (uint32_t)(kt * RB), 0, 0);
     }
   };
 
