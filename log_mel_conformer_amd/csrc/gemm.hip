@@ -608,10 +608,11 @@ __device__ __forceinline__ int swz_rb(int row, int c) {
 // FB is the number of register sets for the MFMA fragments. With two, the
 // reads of the next substep are in flight under the MFMAs of the current
 // one; with one, each substep reads its fragments and then multiplies,
-// which saves (MT + NTL) * 4 registers a lane. That fits a 192x256 tile's
-// four wavefronts in 256 registers (accumulators included), so with a
-// two-stage ring two blocks share a CU and each SIMD runs two wavefronts
-// that hide each other's waits.
+// which saves (MT + NTL) * 4 registers a lane. That fits a 96x128
+// wavefront tile in 256 registers (accumulators included), so each SIMD
+// runs two such wavefronts that hide each other's waits: eight of them in
+// one 384x256 block, or four in each of two 192x256 blocks that share a CU
+// (two 64-byte stages, 56 KB of LDS each).
 template <typename T, typename TO, int BM, int BN, int WM, int WN, int RB, int STAGES, int EPI,
           int OCC, int GM, int FB>
 __global__ void __launch_bounds__(WM * WN * 64, OCC) k_gemm_dl(GemmParams p) {
@@ -880,12 +881,14 @@ hipError_t dispatch_f32(int epi, int aload, const GemmParams& p, hipStream_t s) 
 }
 
 // bf16 operands: direct-to-LDS pipelined kernels; the tile shape follows
-// the row count, the output width (tiles per wave of 256 CUs) and the depth
-// of K.
-//  wide   (N % 256 == 0, N >= 2048): 256x256, 8 wavefronts of 128x64, two 128-byte stages
-//  paired (other N % 256 == 0, no residual add): 192x256, 4 wavefronts of 96x128 with one
-//         fragment set, two 64-byte stages, two blocks per CU
-//  narrow (otherwise):               256x128, 8 wavefronts of 64x64, two blocks per CU
+// the row count, the output width (tiles per wave of 256 CUs) and the
+// epilogue.
+//  N a multiple of 1024, no residual add: 384x256, 8 wavefronts of 96x128
+//         with one fragment set, two 128-byte stages (the whole 160 KB of LDS)
+//  other N % 256 == 0, no residual add: paired 192x256 blocks, 4 wavefronts
+//         of 96x128 with one fragment set, two 64-byte stages, two blocks per CU
+//  otherwise (the fp32 residual add): 256x128, 8 wavefronts of 64x64, two
+//         blocks per CU
 template <int EPI, typename TO>
 hipError_t run_bf16(const GemmParams& p, hipStream_t s) {
   // fewer rows (the LFM2A encoder's 12032 tokens): the shapes below leave
@@ -897,15 +900,20 @@ hipError_t run_bf16(const GemmParams& p, hipStream_t s) {
     if (p.N >= 2048) return run_dl<bf16, TO, 256, 128, 4, 2, 64, 3, EPI, 2, 2>(p, s);
     return run_dl<bf16, TO, 128, 128, 2, 2, 64, 3, EPI, 3, 4>(p, s);
   }
-  // measured inside the encoder (24000 rows): 256x256 tiles in bands of 4
-  // row tiles for the wide projections; paired 192x256 blocks for FFN W2
-  // (208 -> 184 us against one 192x256 block per CU with double-buffered
-  // fragments and three stages), the attention post projection (67 -> 58)
-  // and the head's projections (85 -> 75 on average); the fp32 residual
-  // add of linear_end measured 100 -> 103 that way, the wide ones 1-5%
-  // slower, so they keep their shapes
-  if (p.N % 256 == 0 && p.N >= 2048)
-    return run_dl<bf16, TO, 256, 256, 2, 4, 128, 2, EPI, 1, 4>(p, s);
+  // measured inside the encoder (24000 rows), against the shapes before:
+  // - 384x256 tiles (in bands of 4 row tiles) against 256x256 tiles of
+  //   eight 128x64 wavefronts: q|k|v 165 -> 156 us (752 tiles in 2.9 rounds
+  //   of the CUs instead of 1128 in 4.4), the GLU projection 103.5 -> 100.7,
+  //   FFN W1 the same; against paired 192x256 blocks: FFN W2 180 -> 170.6,
+  //   the attention post projection 56.3 -> 54.2;
+  // - paired 192x256 blocks against one 192x256 block per CU with two
+  //   fragment sets and three stages: FFN W2 208 -> 184, post 67 -> 58, the
+  //   head's projections 85 -> 75 on average; for the head's 512- and
+  //   1536-column outputs 384x256 tiles leave CUs idle (126 and 378 tiles);
+  // - linear_end's fp32 residual add measured 98.7 us in 256x128 blocks,
+  //   101.4 in 384x256 tiles and 103 in paired 192x256 blocks.
+  if (p.N % 1024 == 0 && EPI != EPI_RESID)
+    return run_dl<bf16, TO, 384, 256, 4, 2, 128, 2, EPI, 1, 4, 1>(p, s);
   if (p.N % 256 == 0 && EPI != EPI_RESID)
     return run_dl<bf16, TO, 192, 256, 2, 2, 64, 2, EPI, 2, 4, 1>(p, s);
   return run_dl<bf16, TO, 256, 128, 4, 2, 64, 3, EPI, 2, 2>(p, s);
