@@ -749,7 +749,11 @@ __global__ void __launch_bounds__(WM * WN * 64, OCC) k_gemm_dl(GemmParams p) {
   // duration; spread out, they hide under the MFMAs.
   constexpr int NMFMA = MT * NTL, NLOAD = MT + NTL;
   static_assert(NLOAD <= NMFMA, "interleave needs an MFMA per read");
+  // A wavefront runs its MFMA run at raised priority, so the SIMD's other
+  // wavefront, reading fragments or waiting, does not take issue slots from
+  // it (FFN W2 170.1 -> 167.0 us, the LFM2A step 8.16 -> 8.10 ms).
   auto mfmas = [&](int cur, int nreads, int nloads) {
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int i = 0; i < MT; ++i)
 #pragma unroll
@@ -768,6 +772,7 @@ __global__ void __launch_bounds__(WM * WN * 64, OCC) k_gemm_dl(GemmParams p) {
       }
     }
     __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(0);
   };
   // Every iteration but the last publishes the next stage before its last
   // substep; the last iteration is peeled so the loop body has no branch.
