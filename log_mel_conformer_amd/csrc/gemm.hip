@@ -748,7 +748,7 @@ __global__ void __launch_bounds__(WM * WN * 64, OCC) k_gemm_dl(GemmParams p) {
   // loads back to back would stall the wavefront's issue for their whole
   // duration; spread out, they hide under the MFMAs.
   constexpr int NMFMA = MT * NTL, NLOAD = MT + NTL;
-  static_assert(NLOAD <= NMFMA, "interleave needs an MFMA per read");
+  static_assert(FB == 1 || NLOAD <= NMFMA, "interleave needs an MFMA per read");
   // A wavefront runs its MFMA run at raised priority, so the SIMD's other
   // wavefront, reading fragments or waiting, does not take issue slots from
   // it (FFN W2 170.1 -> 167.0 us, the LFM2A step 8.16 -> 8.10 ms).
@@ -898,13 +898,14 @@ template <int EPI, typename TO>
 hipError_t run_bf16(const GemmParams& p, hipStream_t s) {
   // fewer rows (the LFM2A encoder's 12032 tokens): the shapes below leave
   // CUs idle (a 512-column output in 192x256 tiles is 126 tiles for 256
-  // CUs). Measured inside that encoder: 256x128 tiles, two blocks per CU,
-  // for outputs of 2048 columns or more, else 128x128 tiles (four
-  // wavefronts of 64x64, three blocks per CU)
-  if (p.M < 16384) {
-    if (p.N >= 2048) return run_dl<bf16, TO, 256, 128, 4, 2, 64, 3, EPI, 2, 2>(p, s);
-    return run_dl<bf16, TO, 128, 128, 2, 2, 64, 3, EPI, 3, 4>(p, s);
-  }
+  // CUs), and a 512-column output in 128x128 tiles is still only 376 tiles.
+  // Those run latency-bound, so each tile gets eight 32x64 wavefronts with
+  // one fragment set (three blocks per CU): measured inside that encoder
+  // against four 64x64 wavefronts (and 256x128 blocks for 2048 columns),
+  // the step went from 8.34 to 7.67-7.84 ms (feed-forward down 52.6 -> 46.7
+  // us, the attention projections 28.4 -> 23.5, the convolution module's
+  // 27.8 -> 23.8)
+  if (p.M < 16384) return run_dl<bf16, TO, 128, 128, 4, 2, 64, 3, EPI, 3, 4, 1>(p, s);
   // measured inside the encoder (24000 rows), against the shapes before:
   // - 384x256 tiles (in bands of 4 row tiles) against 256x256 tiles of
   //   eight 128x64 wavefronts: q|k|v 165 -> 156 us (752 tiles in 2.9 rounds
