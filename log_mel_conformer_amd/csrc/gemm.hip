@@ -918,8 +918,12 @@ hipError_t run_bf16(const GemmParams& p, hipStream_t s) {
   //   1536-column outputs 384x256 tiles leave CUs idle (126 and 378 tiles);
   // - linear_end's fp32 residual add measured 98.7 us in 256x128 blocks,
   //   101.4 in 384x256 tiles and 103 in paired 192x256 blocks.
-  if (p.N % 1024 == 0 && EPI != EPI_RESID)
+  // - bands of 8 row tiles for the 4096-deep FFN W2 (167 -> 164 us against
+  //   bands of 4; the others are 1-2% slower that way).
+  if (p.N % 1024 == 0 && EPI != EPI_RESID) {
+    if (p.K >= 2048) return run_dl<bf16, TO, 384, 256, 4, 2, 128, 2, EPI, 1, 8, 1>(p, s);
     return run_dl<bf16, TO, 384, 256, 4, 2, 128, 2, EPI, 1, 4, 1>(p, s);
+  }
   if (p.N % 256 == 0 && EPI != EPI_RESID)
     return run_dl<bf16, TO, 192, 256, 2, 2, 64, 2, EPI, 2, 4, 1>(p, s);
   return run_dl<bf16, TO, 256, 128, 4, 2, 64, 3, EPI, 2, 2>(p, s);
