@@ -219,14 +219,13 @@ template <typename TS> __device__ __forceinline__ void get4s(const unsigned char
   }
 }
 
-// LDS bytes of one 32-row slab per wavefront row in the staged epilogue
-// (none for the direct SiLU and GLU epilogues); a kernel whose stage ring
-// is smaller than that gets the larger LDS array.
+// LDS bytes of one 32-row slab per wavefront row in the staged epilogue; a
+// kernel whose stage ring is smaller than that gets the larger LDS array.
 template <typename TO, int EPI, int BN, int WM>
 constexpr int staged_slab_bytes() {
   constexpr int es = EPI == EPI_RESID ? 4 : (int)sizeof(TO);
   constexpr int outn = EPI == EPI_GLU ? BN / 2 : BN;
-  return (EPI == EPI_SILU || EPI == EPI_GLU) ? 0 : WM * 32 * (outn * es + 4 * es);
+  return WM * 32 * (outn * es + 4 * es);
 }
 
 constexpr int staged_slabs(int mt, int slab, int ldsb) {
@@ -287,14 +286,21 @@ __device__ __forceinline__ void epilogue_staged(const GemmParams& p,
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
             const int c = wn * WOUT + jp * 32 + g * 8 + h * 4;
+            float ba[4] = {0.f, 0.f, 0.f, 0.f}, bb[4] = {0.f, 0.f, 0.f, 0.f};
+            if (p.bias) {  // 16-byte loads of the a and b halves' biases
+              const float4 va = *(const float4*)(p.bias + ocol0 + c);
+              const float4 vb = *(const float4*)(p.bias + p.glu_d + ocol0 + c);
+              ba[0] = va.x; ba[1] = va.y; ba[2] = va.z; ba[3] = va.w;
+              bb[0] = vb.x; bb[1] = vb.y; bb[2] = vb.z; bb[3] = vb.w;
+            }
             float o[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               float a = clampf(acc[i][2 * jp][4 * g + e], lo, hi);
               float b = clampf(acc[i][2 * jp + 1][4 * g + e], lo, hi);
               if (p.bias) {
-                a += p.bias[ocol0 + c + e];
-                b += p.bias[p.glu_d + ocol0 + c + e];
+                a += ba[e];
+                b += bb[e];
               }
               o[e] = a * sigmoidf_(b);
             }
@@ -842,14 +848,11 @@ __global__ void __launch_bounds__(WM * WN * 64, OCC) k_gemm_dl(GemmParams p) {
     }
   }
   }
-  // Staging wins where the epilogue is light (plain store, residual add,
-  // bias); SiLU and GLU spend enough arithmetic per value that storing
-  // straight from registers, overlapped with that arithmetic, is faster.
-  if constexpr (EPI == EPI_SILU || EPI == EPI_GLU)
-    epilogue<TO, MT, NTL, EPI>(p, acc, m0 + wm * WTM, n0 + wn * WTN, seg, lane);
-  else
-    epilogue_staged<TO, BM, BN, WM, WN, EPI, SMEM>(p, acc, smem, m0, n0, wm, wn, seg,
-                                                            wave, lane);
+  // Every epilogue is staged through LDS, SiLU and GLU included: with the
+  // 384x256 tiles that took FFN W1 from 218 to 208.5 us and the GLU
+  // projection from 101.7 to 98.2 against storing them straight from
+  // registers (which the 256x256 tiles had preferred).
+  epilogue_staged<TO, BM, BN, WM, WN, EPI, SMEM>(p, acc, smem, m0, n0, wm, wn, seg, wave, lane);
 }
 
 template <typename T, typename TO, int BM, int BN, int WM, int WN, int RB, int STAGES, int EPI,
