@@ -1,0 +1,72 @@
+"""CPU checks of the benchmark's host logic: the one-GPU refusal, the FLOP
+counts behind the roofline, and the rule that a stored HBM-traffic record
+counts only while the kernel sources it was measured on are unchanged."""
+import json
+import os
+import subprocess
+import sys
+import types
+
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU only" in r.stderr and "asked for 2" in r.stderr
+
+
+def test_gemm_flops_per_launch():
+    cfg = types.SimpleNamespace(hidden=1024, ff=4096)
+    T = 24000
+    # 2 M N K for each projection of a layer
+    assert bench.gemm_flops_per_launch("gemm_ffn1", T, cfg) == 2.0 * T * 4096 * 1024
+    assert bench.gemm_flops_per_launch("gemm_ffn2", T, cfg) == 2.0 * T * 1024 * 4096
+    assert bench.gemm_flops_per_launch("gemm_qkv", T, cfg) == 2.0 * T * 3072 * 1024
+    assert bench.gemm_flops_per_launch("gemm_lcstart", T, cfg) == 2.0 * T * 2048 * 1024
+    # 201.3 GFLOP for the 32 x 30 s workload's FFN W1
+    assert abs(bench.gemm_flops_per_launch("gemm_ffn1", T, cfg) / 1e9 - 201.3) < 0.05
+
+
+def _record(tmp_path, kclass, workload, sha, hbm):
+    prof = tmp_path / "profiles"
+    prof.mkdir(exist_ok=True)
+    rec = {"kernel_class": kclass, "workload": workload, "hbm_bytes_per_launch": hbm,
+           "sources_sha256": sha}
+    (prof / f"traffic_{kclass}_{workload}.md").write_text(
+        "# record\n\n```json\n" + json.dumps(rec, indent=1) + "\n```\n")
+
+
+def test_traffic_record_needs_matching_sources(tmp_path, monkeypatch):
+    csrc = tmp_path / "log_mel_conformer_amd" / "csrc"
+    csrc.mkdir(parents=True)
+    for f in ("gemm.hip", "launch.h", "common.h"):
+        (csrc / f).write_text(f"// {f}\n")
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    sha = bench.sources_sha256("gemm_ffn1")
+    _record(tmp_path, "gemm_ffn1", "batch32", sha, 12345)
+    assert bench.recorded_traffic("gemm_ffn1", "batch32") == 12345.0
+    # no record for another workload
+    assert bench.recorded_traffic("gemm_ffn1", "lfm2a32") is None
+    # any change to a source the kernel is built from voids the record
+    (csrc / "common.h").write_text("// common.h, edited\n")
+    assert bench.recorded_traffic("gemm_ffn1", "batch32") is None
+
+
+def test_committed_records_name_their_kernel():
+    """Every committed traffic record parses and names its kernel class and
+    workload (whether it is still valid depends on the sources)."""
+    prof = os.path.join(ROOT, "profiles")
+    names = [n for n in os.listdir(prof) if n.startswith("traffic_") and n.endswith(".md")]
+    assert names
+    for n in names:
+        text = open(os.path.join(prof, n)).read()
+        blocks = text.split("```json")[1:]
+        assert blocks, n
+        rec = json.loads(blocks[-1].split("```")[0])
+        assert n == f"traffic_{rec['kernel_class']}_{rec['workload']}.md"
+        assert rec["hbm_bytes_per_launch"] > 0 and len(rec["sources_sha256"]) == 64
