@@ -231,6 +231,34 @@ def test_layer_packed_positions_bf16():
         off += n
 
 
+@pytest.mark.parametrize("total", [16383, 16384, 16385])
+def test_layer_row_count_across_tile_rules_bf16(total):
+    """The bf16 projections pick their tiles by row count: below 16384 rows
+    128x128 tiles of eight wavefronts, from 16384 rows 384x256 tiles,
+    paired 192x256 blocks or 256x128 blocks (the residual add). One layer
+    on packed clips totalling 16383, 16384 and 16385 rows (ragged tails in
+    every tile shape); the short clips and the last one, whose rows sit in
+    the final partial row tile, against the oracle."""
+    say(f"[gpu] conformer_layer: {total} packed rows around the 16384-row tile rule, bf16")
+    W = weights(1, bf16=True)
+    m = ae.Model(W, dtype="bf16")
+    rng = np.random.default_rng(total)
+    lens = [3, 40, total - 3 - 40 - 57, 57]
+    h0 = (0.5 * rng.standard_normal((total, 1024))).astype(np.float32)
+    pos = np.concatenate([np.arange(n) for n in lens]).astype(np.int32)
+    h = cuda(h0)
+    ae.conformer_layer(m, 0, h, cuda(pos, torch.int32))
+    g = h.cpu().numpy()
+    offs = np.concatenate([[0], np.cumsum(lens)])
+    for i in (0, 1, 3):
+        a, b = offs[i], offs[i + 1]
+        want = oracle.conformer_layer(h0[a:b], W["layers"][0], np.arange(b - a, dtype=np.int32))
+        r = rel_l2(g[a:b], want)
+        say(f"    clip of {b - a} rows at {a}: rel {r:.3e}")
+        assert r <= BF16_TOL, (total, i, r)
+    assert np.all(np.isfinite(g))
+
+
 def test_layer_clamps_and_softcap_bind_fp32():
     """Bounds of +-0.5 make every clamp bind; large q weights and
     per_dim_scale above 20 (softplus pass-through) push logits past the
