@@ -7,13 +7,25 @@ residual stream; random-init weights. A step is one ae_encode over the
 batch, inputs already resident in HBM. Prints one JSON line.
 
   python bench.py [--gpus 1] [--steps 20] [--warmup 5]
-                  [--workload batch32|batch32q8|frontend256|ragged64|resample48k|merge32|
-                              lfm2a32]
-                  [--kernel gemm_ffn1] [--no-cpu-baseline] [--copy-probe]
+                  [--workload batch32|batch32q8|ragged64|frontend256|tone1s|clip30f32|
+                              resample48k|merge32|lfm2a32]
+                  [--kernel gemm_ffn1] [--no-cpu-baseline] [--cpu-threads N]
+                  [--no-kernel-table] [--copy-probe]
 
---copy-probe runs one plain 256 MiB device-to-device copy after the timed
-region; under rocprofv3 --pmc it is the calibration for FETCH_SIZE and
-WRITE_SIZE (the counters' reading for a known byte count).
+Workloads of the encoder: batch32 (32 x 30 s, bf16), ragged64 (64 clips of
+1-30 s, bf16), frontend256 (the log-mel front end over 256 x 30 s, fp32),
+tone1s (1 s tone: log-mel, subsampler and one Conformer layer, fp32),
+clip30f32 (one 30 s clip, 12 layers and the head, fp32), batch32q8
+(batch32 with int8 projections).
+
+The timed region carries HIP events around the launches of one kernel
+class (--kernel; the roofline object). After it: the same steps with no
+events (ms_per_step_no_events), and for the encoder workloads one short
+pass per kernel class with events around that class alone, for the
+per-kernel roofline table ("kernels"). --copy-probe runs one plain 256 MiB
+device-to-device copy after the timed region; under rocprofv3 --pmc it is
+the calibration for FETCH_SIZE and WRITE_SIZE. --cpu-threads sets the BLAS
+threads of the oracle baseline (default: every core this process may use).
 """
 import argparse
 import hashlib
@@ -89,17 +101,41 @@ def recorded_traffic(kclass, workload):
     return None
 
 
-def cpu_baseline(clip, W, seconds):
-    """The oracle (f64 numpy) on one clip of the workload, timed on the host."""
+def host_cpu():
+    """The host CPU's model name and the cores this process may run on."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return model, len(os.sched_getaffinity(0))
+
+
+def oracle_run(fn, threads):
+    """fn() under a BLAS thread limit; returns (seconds, threads used, CPU)."""
+    from threadpoolctl import threadpool_limits
+    model, avail = host_cpu()
+    n = threads or avail
+    with threadpool_limits(limits=n):
+        t0 = time.perf_counter()
+        fn()
+        dt = time.perf_counter() - t0
+    return dt, n, model
+
+
+def cpu_baseline(clips, W, seconds, threads, layers=None, with_head=True, what=None):
+    """The oracle (f64 numpy) on a sample of the workload's clips."""
     import oracle
-    from threadpoolctl import threadpool_info
-    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    t0 = time.perf_counter()
-    oracle.encode_clips([clip], W)
-    dt = time.perf_counter() - t0
-    return {"value": seconds / dt, "unit": "audio-s/s", "cores": threads, "kind": "oracle",
-            "sample": f"1 clip of the workload ({seconds:.0f} s, {len(clip)} samples), full "
-                      f"encoder in float64 numpy, {dt:.1f} s wall"}
+    dt, n, model = oracle_run(lambda: oracle.encode_clips(clips, W, layers=layers,
+                                                          with_head=with_head), threads)
+    return {"value": seconds / dt, "unit": "audio-s/s", "cores": n, "kind": "oracle",
+            "cpu": model,
+            "sample": what or (f"{len(clips)} clip(s) of the workload ({seconds:.1f} s of audio), "
+                               f"full encoder in float64 numpy, {dt:.1f} s wall")}
 
 
 def copy_probe(torch):
@@ -182,13 +218,11 @@ def bench_resample(args, torch, ae, synth):
     cpu = None
     if not args.no_cpu_baseline:
         import oracle.resample as ors
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
         c0 = clips[0]
-        t0 = time.perf_counter()
-        ors.to_mono_16k([c0[:, 0], c0[:, 1]], 48000)
-        dt = time.perf_counter() - t0
+        dt, threads, model = oracle_run(lambda: ors.to_mono_16k([c0[:, 0], c0[:, 1]], 48000),
+                                        args.cpu_threads)
         cpu = {"value": 30.0 / dt, "unit": "audio-s/s", "cores": threads, "kind": "oracle",
+               "cpu": model,
                "sample": f"1 clip of the workload (30 s stereo at 48 kHz) through the oracle's "
                          f"mixdown and resampler, float64 numpy, {dt:.1f} s wall"}
     r.close()
@@ -325,12 +359,9 @@ def bench_lfm2a(args, torch, ae, synth):
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline: the LFM2A oracle on one clip")
         from oracle import lfm2a as olfm
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-        c0 = time.perf_counter()
-        olfm.encode(clips[0], W)
-        dt = time.perf_counter() - c0
+        dt, threads, model = oracle_run(lambda: olfm.encode(clips[0], W), args.cpu_threads)
         cpu = {"value": 30.0 / dt, "unit": "audio-s/s", "cores": threads, "kind": "oracle",
+               "cpu": model,
                "sample": f"1 clip of the workload (30 s), the whole LFM2A encoder in float64 "
                          f"numpy, {dt:.1f} s wall"}
     rec = {"metric": "audio-seconds encoded/sec (LFM2A Conformer: front end, stem, 17 blocks, "
@@ -351,16 +382,101 @@ def bench_lfm2a(args, torch, ae, synth):
     print(json.dumps(rec), flush=True)
 
 
+ENCODER_NAMES = {
+    "batch32": "32 clips x 30 s multisine+noise: log-mel, subsampler, 12 Conformer layers, head "
+               "(bf16 MFMA, fp32 accumulation and norms)",
+    "batch32q8": "32 clips x 30 s multisine+noise, the encoder with int8 projections (per-row "
+                 "scales) widened to bf16",
+    "ragged64": "64 clips, 1-30 s pink noise, packed ragged: full encoder, bf16",
+    "frontend256": "256 clips x 30 s white noise: log-mel front end only, fp32",
+    "tone1s": "one 1 s tone (440 Hz + noise): log-mel, subsampler, one Conformer layer, fp32",
+    "clip30f32": "one 30 s multisine clip: full encoder (12 layers + head), fp32",
+}
+
+
+def encoder_work(pl, cfg, es, layers, q8=False):
+    """Algorithmic work per step of each kernel class of ae_encode: (bound,
+    amount, unit) with flops for the matrix-core classes and bytes for the
+    memory-bound ones. es = bytes per stored activation (2 bf16, 4 fp32)."""
+    T = float(pl["token_off"][-1])
+    F = float(pl["frame_off"][-1])
+    T1 = float(pl["row_off"][-1])
+    S = float(pl["sample_off"][-1])
+    d, ff, oh, od = cfg.hidden, cfg.ff, cfg.out_hidden, cfg.out_dim
+    L = layers
+    post = (es + 8 + es) * d           # y in, h read and written, next input out
+    pre = (4 + es) * d                  # h in, normed input out
+    last = (es + 8 + (es if es == 2 else 0)) * d
+    rows = pre + L * (3 * post + pre) - post + last + (4 + es) * oh
+    w = {
+        "logmel": ("hbm", 4.0 * S + 4.0 * 128 * F),
+        "conv0": ("hbm", 4.0 * 128 * F + es * T1 * 64 * 128),
+        "conv1": ("mfma", 2.0 * (32 * T) * 32 * 1152),
+        "gemm_ffn1": ("mfma", L * 2 * 2.0 * T * ff * d),
+        "gemm_ffn2": ("mfma", L * 2 * 2.0 * T * d * ff),
+        "gemm_qkv": ("mfma", L * 2.0 * T * 3 * d * d),
+        "gemm_post": ("mfma", L * 2.0 * T * d * d),
+        "gemm_lcstart": ("mfma", L * 2.0 * T * 2 * d * d),
+        "gemm_lcend": ("mfma", L * 2.0 * T * d * d),
+        "gemm_head": ("mfma", 2.0 * T * d * 1024 + 2.0 * T * oh * d + 2.0 * T * od * oh),
+        "rownorm": ("hbm", T * rows),
+        "attn": ("hbm", L * T * 4 * es * d),
+        "lconv": ("hbm", L * T * 2 * es * d),
+    }
+    if q8:
+        w["dequant"] = ("hbm", L * 3.0 * (2 * ff * d * 2 + 7 * d * d) * 1.0)
+    return w
+
+
+def kernel_table(ae, torch, step, work, steps, peak_mm):
+    """One pass per kernel class with HIP events around its launches alone:
+    average launch time, achieved rate and fraction of the roofline."""
+    out = []
+    for cls, (bound, amount) in work.items():
+        ae.timing_enable(cls)
+        for _ in range(steps):
+            step()
+        torch.cuda.synchronize()
+        launches, kms = ae.timing_read()
+        ae.timing_enable(None)
+        if launches == 0:
+            continue
+        per_step_ms = kms / steps
+        if bound == "mfma":
+            ach = amount / (per_step_ms / 1e3) / 1e12
+            peak, unit = peak_mm, "TFLOP/s"
+        else:
+            ach = amount / (per_step_ms / 1e3) / 1e9
+            peak, unit = PEAK_HBM_GBS, "GB/s"
+        out.append({"kernel": cls, "bound": bound, "launches_per_step": launches // steps,
+                    "avg_us": 1e3 * kms / launches, "ms_per_step": per_step_ms,
+                    "work_per_step": amount, "achieved": ach, "peak": peak, "unit": unit,
+                    "frac": ach / peak})
+    return out
+
+
+def time_steps(step, torch, steps):
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3 / steps
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="batch32",
-                    choices=["batch32", "batch32q8", "frontend256", "ragged64", "resample48k",
-                             "merge32", "lfm2a32"])
-    ap.add_argument("--kernel", default="gemm_ffn1")
+                    choices=["batch32", "batch32q8", "ragged64", "frontend256", "tone1s",
+                             "clip30f32", "resample48k", "merge32", "lfm2a32"])
+    ap.add_argument("--kernel", default=None,
+                    help="kernel class of the roofline object (default: the workload's largest)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-threads", type=int, default=0)
+    ap.add_argument("--no-kernel-table", action="store_true")
     ap.add_argument("--copy-probe", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -379,13 +495,15 @@ def main():
     if args.workload == "merge32":
         return bench_merge(args, torch, ae, synth)
     if args.workload == "lfm2a32":
+        args.kernel = args.kernel or "lfm_gemm_ffn1"
         return bench_lfm2a(args, torch, ae, synth)
-    if args.workload in ("batch32", "batch32q8"):
-        clips = synth.multisine_batch(32)
-    elif args.workload == "ragged64":
-        clips = synth.ragged_batch(64)
-    else:
-        clips = synth.white_batch(256)
+    wl = args.workload
+    clips = {"batch32": lambda: synth.multisine_batch(32),
+             "batch32q8": lambda: synth.multisine_batch(32),
+             "ragged64": lambda: synth.ragged_batch(64),
+             "frontend256": lambda: synth.white_batch(256),
+             "tone1s": lambda: [synth.tone_clip(0)],
+             "clip30f32": lambda: [synth.multisine_clip(0)]}[wl]()
     wave_np, so = synth.pack(clips)
     wave = torch.from_numpy(wave_np).cuda()
     pl = ae.plan(np.diff(so))
@@ -394,25 +512,49 @@ def main():
     frames = int(pl["frame_off"][-1])
 
     W = None
-    if args.workload == "frontend256":
+    model = None
+    work = {}
+    layers = 12
+    if wl == "frontend256":
         mel = torch.empty((frames, 128), dtype=torch.float32, device="cuda")
         step = lambda: ae.logmel(wave, so, out=mel)  # noqa: E731
-        kclass = "logmel"
+        kclass = args.kernel or "logmel"
         dtype = "f32"
+        work = {"logmel": ("hbm", 4.0 * float(pl["sample_off"][-1]) + 4.0 * 128 * frames)}
+        peak_mm = PEAK_F32_TFLOPS
     else:
-        if args.workload == "batch32q8":
+        f32 = wl in ("tone1s", "clip30f32")
+        layers = 1 if wl == "tone1s" else 12
+        if wl == "batch32q8":
             log("[bench] generating weights (12 layers, int8 projections)")
             W, S = synth.make_weights_q8(layers=12)
             model = ae.Model(W, dtype="bf16", scales=S)
         else:
-            log("[bench] generating weights (12 layers, bf16)")
-            W = synth.make_weights(layers=12, bf16=True)
-            model = ae.Model(W, dtype="bf16")
-        out = torch.empty((tokens, 512), dtype=torch.float32, device="cuda")
+            log(f"[bench] generating weights ({layers} layers, {'fp32' if f32 else 'bf16'})")
+            W = synth.make_weights(layers=layers, bf16=not f32)
+            model = ae.Model(W, dtype="f32" if f32 else "bf16")
+        dtype = "f32" if f32 else "bf16"
+        peak_mm = PEAK_F32_TFLOPS if f32 else PEAK_BF16_TFLOPS
         model.workspace(len(clips), frames, tokens)
-        step = lambda: ae.encode(model, wave, so, out=out)  # noqa: E731
-        kclass = args.kernel
-        dtype = "bf16"
+        if wl == "tone1s":
+            # the configuration's three stages: log-mel, subsampler, one layer
+            mel = torch.empty((frames, 128), dtype=torch.float32, device="cuda")
+            h = torch.empty((tokens, model.cfg.hidden), dtype=torch.float32, device="cuda")
+            pos = torch.arange(tokens, dtype=torch.int32, device="cuda")
+
+            def step():
+                ae.logmel(wave, so, out=mel)
+                ae.subsample(model, mel, pl["frame_off"], out=h)
+                ae.conformer_layer(model, 0, h, pos)
+            work = encoder_work(pl, model.cfg, 4, 1)
+            work.pop("gemm_head")
+            work["rownorm"] = ("hbm", tokens * ((4 + 4) * 1024 + 3 * (4 + 8 + 4) * 1024
+                                                + (4 + 4) * 1024 + (4 + 8) * 1024))
+        else:
+            out = torch.empty((tokens, 512), dtype=torch.float32, device="cuda")
+            step = lambda: ae.encode(model, wave, so, out=out)  # noqa: E731
+            work = encoder_work(pl, model.cfg, 4 if f32 else 2, layers, q8=(wl == "batch32q8"))
+        kclass = args.kernel or "gemm_ffn1"
 
     log(f"[bench] warmup {args.warmup}")
     for _ in range(args.warmup):
@@ -420,73 +562,75 @@ def main():
     torch.cuda.synchronize()
     log(f"[bench] timing {args.steps} steps (events around {kclass})")
     ae.timing_enable(kclass)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
+    ms = time_steps(step, torch, args.steps)
     launches, kms = ae.timing_read()
     ae.timing_enable(None)
-    ms = (t1 - t0) * 1e3 / args.steps
+    log("[bench] the same steps without events")
+    ms_plain = time_steps(step, torch, args.steps)
     if args.copy_probe:
         copy_probe(torch)
     value = audio_s / (ms / 1e3)
     avg_ms = kms / max(launches, 1)
 
-    if kclass == "logmel":
-        # algorithmic bytes: every input sample read once, every log-mel value written once
-        per_launch = 4.0 * float(pl["sample_off"][-1]) + 4.0 * 128 * frames
+    bound, amount = work[kclass]
+    per_launch = amount / max(launches // args.steps, 1)
+    if bound == "hbm":
         achieved = per_launch / (avg_ms / 1e3) / 1e9
-        roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": achieved / PEAK_HBM_GBS,
-                "traffic": recorded_traffic(kclass, args.workload), "kernel": "k_logmel",
-                "avg_ms": avg_ms, "launches": launches}
+        roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
     else:
-        flops = gemm_flops_per_launch(kclass, tokens, model.cfg)
-        achieved = flops / (avg_ms / 1e3) / 1e12
-        roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
-                "traffic": recorded_traffic(kclass, args.workload),
-                "kernel": kclass, "avg_ms": avg_ms, "launches": launches}
+        achieved = per_launch / (avg_ms / 1e3) / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": peak_mm, "unit": "TFLOP/s"}
+    roof.update({"frac": achieved / roof["peak"],
+                 "traffic": recorded_traffic(kclass, wl), "kernel": kclass,
+                 "work_per_launch": per_launch, "avg_ms": avg_ms, "launches": launches})
+
+    table = None
+    if not args.no_kernel_table and len(work) > 1:
+        log("[bench] per-kernel events, one class at a time")
+        table = kernel_table(ae, torch, step, work, 3, peak_mm)
 
     cpu = None
-    if not args.no_cpu_baseline and W is not None:
-        log("[bench] cpu baseline: oracle on one clip")
-        if args.workload == "batch32q8":
-            # the oracle runs the widened weights bf16(float32(q) * s)
-            from oracle import quant
-            W = {**W, "layers": [{**L, **{k: quant.dequantize_rows(L[k], sc[k]) for k in sc}}
-                                 for L, sc in zip(W["layers"], S)]}
-        cpu = cpu_baseline(clips[0], W, len(clips[0]) / 16000.0)
-    elif not args.no_cpu_baseline:
-        import oracle
-        from threadpoolctl import threadpool_info
-        t0 = time.perf_counter()
-        n = 0
-        while time.perf_counter() - t0 < 10.0 and n < len(clips):
-            oracle.log_mel(clips[n])
-            n += 1
-        dt = time.perf_counter() - t0
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-        cpu = {"value": n * 30.0 / dt, "unit": "audio-s/s", "cores": threads, "kind": "oracle",
-               "sample": f"log-mel of {n} of the 256 clips in float64 numpy"}
+    if not args.no_cpu_baseline:
+        if wl == "frontend256":
+            import oracle
+            log("[bench] cpu baseline: oracle log-mel on a sample of the clips")
+            n = 3
+            dt, threads, cpu_model = oracle_run(lambda: [oracle.log_mel(c) for c in clips[:n]],
+                                                args.cpu_threads)
+            cpu = {"value": n * 30.0 / dt, "unit": "audio-s/s", "cores": threads,
+                   "kind": "oracle", "cpu": cpu_model,
+                   "sample": f"log-mel of {n} of the 256 clips in float64 numpy, {dt:.1f} s wall"}
+        else:
+            Wo = W
+            if wl == "batch32q8":
+                # the oracle runs the widened weights bf16(float32(q) * s)
+                from oracle import quant
+                Wo = {**W, "layers": [{**L, **{k: quant.dequantize_rows(L[k], sc[k]) for k in sc}}
+                                      for L, sc in zip(W["layers"], S)]}
+            if wl == "ragged64":
+                # a bounded sample: the clips nearest the batch's mean length
+                order = np.argsort(np.abs(np.diff(so) - np.mean(np.diff(so))))
+                sample = [clips[i] for i in order[:2]]
+            else:
+                sample = clips[:1]
+            secs = sum(len(c) for c in sample) / 16000.0
+            log(f"[bench] cpu baseline: oracle on {len(sample)} clip(s), {secs:.1f} s of audio")
+            cpu = cpu_baseline(sample, Wo, secs, args.cpu_threads,
+                               layers=layers, with_head=(wl != "tone1s"))
+            if wl == "tone1s":
+                cpu["sample"] = ("the whole workload (1 s clip: log-mel, subsampler, one layer; "
+                                 "the oracle also runs the head) in float64 numpy")
 
-    names = {"batch32": "32 clips x 30 s multisine+noise: log-mel, subsampler, 12 Conformer "
-                        "layers, head (bf16 MFMA, fp32 accumulation and norms)",
-             "batch32q8": "32 clips x 30 s multisine+noise, the encoder with int8 projections "
-                          "(per-row scales) widened to bf16 per layer per forward",
-             "ragged64": "64 clips, 1-30 s pink noise, packed ragged: full encoder, bf16",
-             "frontend256": "256 clips x 30 s white noise: log-mel front end only, fp32"}
     rec = {"metric": METRIC, "value": value, "unit": "audio-s/s", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+           "ms_per_step_no_events": ms_plain,
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dtype,
            "data": "synthetic (seeded waveforms, random-init weights)",
-           "config": {"workload": names[args.workload], "global_batch": len(clips),
+           "config": {"workload": ENCODER_NAMES[wl], "global_batch": len(clips),
                       "seq_len": int(max(np.diff(pl["token_off"]))) if tokens else 0,
                       "tokens": tokens, "frames": frames, "audio_seconds": audio_s,
                       "tokens_per_s": tokens / (ms / 1e3), "parallelism": "none (1 GPU)"},
-           "roofline": roof, "cpu_baseline": cpu}
+           "roofline": roof, "kernels": table, "cpu_baseline": cpu}
     add_copy_denominator(rec["roofline"], torch)
     print(json.dumps(rec), flush=True)
 

@@ -130,6 +130,13 @@ int64_t ae_num_tokens(int64_t n_samples);
  * Any output may be NULL. Negative lengths are AE_ERR_INVALID. */
 ae_status ae_plan(const int64_t* n_samples, int32_t B, int64_t* sample_off,
                   int64_t* frame_off, int64_t* row_off, int64_t* token_off);
+/* The same prefix sums from a packed log-mel layout (what ae_subsample
+ * receives): frame_off host int64 [B+1], non-decreasing from 0, at most
+ * 2999 frames a clip; row_off (conv0 rows, ceil(F/2)) and token_off
+ * (ceil(ceil(F/2)/2)) host int64 [B+1] written by the call, either NULL.
+ * AE_ERR_INVALID / AE_ERR_SHAPE as ae_subsample refuses the offsets. */
+ae_status ae_plan_frames(const int64_t* frame_off, int32_t B, int64_t* row_off,
+                         int64_t* token_off);
 
 /* --- model ----------------------------------------------------------- */
 

@@ -112,6 +112,11 @@ int64_t lfm2a_num_tokens(int64_t n_samples);
  * is allowed: no frames, no tokens). */
 ae_status lfm2a_plan(const int64_t* n_samples, int32_t B, int64_t* sample_off,
                      int64_t* frame_off, int64_t* token_off);
+/* Token prefix sums from a packed feature layout (what lfm2a_stem
+ * receives): frame_off host int64 [B+1], non-decreasing from 0; token_off
+ * host int64 [B+1] written by the call (clip i: its frame count through the
+ * stem's three stride-2 convolutions). AE_ERR_INVALID for bad offsets. */
+ae_status lfm2a_plan_frames(const int64_t* frame_off, int32_t B, int64_t* token_off);
 
 /* --- front end -------------------------------------------------------- */
 

@@ -99,6 +99,7 @@ def lib():
             "ae_num_frames": (C.c_int64, [C.c_int64]),
             "ae_num_tokens": (C.c_int64, [C.c_int64]),
             "ae_plan": (C.c_int, [i64p, C.c_int32, i64p, i64p, i64p, i64p]),
+            "ae_plan_frames": (C.c_int, [i64p, C.c_int32, i64p, i64p]),
             "ae_model_create": (C.c_int, [C.POINTER(Config), C.POINTER(Weights), C.c_int, _P,
                                           C.POINTER(_P)]),
             "ae_model_create_q8": (C.c_int, [C.POINTER(Config), C.POINTER(Weights),
@@ -156,6 +157,29 @@ def _ptr(t):
     return C.c_void_p(t.data_ptr()) if t is not None else None
 
 
+def _dev(t, name, dtype, numel=None, shape=None):
+    """Refuse, before any launch, a tensor the kernels would read or write
+    out of bounds: not a tensor on the current GPU, the wrong dtype, not
+    contiguous, or smaller than the call's sizes."""
+    import torch
+    if not torch.is_tensor(t):
+        raise AeError(AE_ERR_INVALID, f"{name}: a torch tensor is required, got {type(t).__name__}")
+    if t.device.type != "cuda":
+        raise AeError(AE_ERR_INVALID, f"{name}: must be a GPU tensor, not on {t.device}")
+    if t.device.index != torch.cuda.current_device():
+        raise AeError(AE_ERR_INVALID, f"{name}: on {t.device}, not the current GPU "
+                                      f"cuda:{torch.cuda.current_device()}")
+    if t.dtype != dtype:
+        raise AeError(AE_ERR_INVALID, f"{name}: dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise AeError(AE_ERR_INVALID, f"{name}: must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise AeError(AE_ERR_SHAPE, f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if numel is not None and t.numel() < numel:
+        raise AeError(AE_ERR_SHAPE, f"{name}: {t.numel()} elements, the call needs {numel}")
+    return t
+
+
 # ------------------------------------------------------------------ sizes
 
 def default_config(**over) -> Config:
@@ -181,6 +205,26 @@ def plan(lengths):
     outs = [np.zeros(B + 1, np.int64) for _ in range(4)]
     _check(lib().ae_plan(p, B, *[o.ctypes.data_as(C.POINTER(C.c_int64)) for o in outs]))
     return dict(sample_off=outs[0], frame_off=outs[1], row_off=outs[2], token_off=outs[3])
+
+
+def plan_frames(frame_off):
+    """conv0-row and token prefix sums of a packed log-mel layout."""
+    fo, fp = _i64(frame_off)
+    B = len(fo) - 1
+    outs = [np.zeros(B + 1, np.int64) for _ in range(2)]
+    _check(lib().ae_plan_frames(fp, B, *[o.ctypes.data_as(C.POINTER(C.c_int64)) for o in outs]))
+    return dict(frame_off=fo, row_off=outs[0], token_off=outs[1])
+
+
+def _sample_plan(sample_off):
+    """Lengths from packed sample offsets, then ae_plan."""
+    so, sp = _i64(sample_off)
+    if len(so) < 1 or so[0] != 0:
+        raise AeError(AE_ERR_INVALID, "sample_off must start at 0")
+    lens = np.diff(so)
+    if np.any(lens < 0):
+        raise AeError(AE_ERR_INVALID, "sample_off must be non-decreasing")
+    return so, sp, plan(lens)
 
 
 # ------------------------------------------------------------------ model
@@ -305,12 +349,13 @@ class Model:
 def logmel(wave, sample_off, out=None):
     """wave: cuda float32 [sum N]; sample_off: host int64 [B+1] -> [sum F, 128]."""
     import torch
-    so, sp = _i64(sample_off)
+    so, sp, pl = _sample_plan(sample_off)
     B = len(so) - 1
-    lens = np.diff(so)
-    F = int(sum(num_frames(n) for n in lens))
+    F = int(pl["frame_off"][-1])
+    _dev(wave, "wave", torch.float32, numel=int(so[-1]))
     if out is None:
         out = torch.empty((F, 128), dtype=torch.float32, device=wave.device)
+    _dev(out, "out", torch.float32, shape=(F, 128))
     ws = torch.empty(max(int(lib().ae_logmel_workspace_bytes(B)), 256), dtype=torch.uint8,
                      device=wave.device)
     _check(lib().ae_logmel(_ptr(wave), sp, B, _ptr(out), _ptr(ws), ws.numel(), _stream()))
@@ -320,12 +365,15 @@ def logmel(wave, sample_off, out=None):
 def subsample(model: Model, mel, frame_off, out=None):
     """mel: cuda float32 [sum F, 128]; frame_off host int64 [B+1] -> [sum T, hidden]."""
     import torch
-    fo, fp = _i64(frame_off)
+    pf = plan_frames(frame_off)
+    fo, fp = _i64(pf["frame_off"])
     B = len(fo) - 1
     F = int(fo[-1])
-    T = int(sum((-(-(-(-int(f) // 2)) // 2)) for f in np.diff(fo)))
+    T = int(pf["token_off"][-1])
+    _dev(mel, "mel", torch.float32, numel=F * 128)
     if out is None:
         out = torch.empty((T, model.cfg.hidden), dtype=torch.float32, device=mel.device)
+    _dev(out, "out", torch.float32, shape=(T, model.cfg.hidden))
     ws = model.workspace(B, F, T)
     _check(lib().ae_subsample(model.handle, _ptr(mel), fp, B, _ptr(out), _ptr(ws), ws.numel(),
                               _stream()))
@@ -334,7 +382,12 @@ def subsample(model: Model, mel, frame_off, out=None):
 
 def conformer_layer(model: Model, layer: int, h, pos):
     """In place on h: cuda float32 [n, hidden]; pos: cuda int32 [n]."""
+    import torch
+    if not torch.is_tensor(h) or h.dim() != 2:
+        raise AeError(AE_ERR_SHAPE, "h: a 2-D tensor [n, hidden] is required")
     n = h.shape[0]
+    _dev(h, "h", torch.float32, shape=(n, model.cfg.hidden))
+    _dev(pos, "pos", torch.int32, shape=(n,))
     ws = model.workspace(1, 0, n)
     _check(lib().ae_conformer_layer(model.handle, layer, _ptr(h), _ptr(pos), n, _ptr(ws),
                                     ws.numel(), _stream()))
@@ -345,12 +398,13 @@ def encode(model: Model, wave, sample_off, out=None, trace: bool = False):
     """Soft tokens [sum T, out_dim] of the packed clips. With trace=True also
     returns [subsampler output, each layer's output, output_proj + bias]."""
     import torch
-    so, sp = _i64(sample_off)
+    so, sp, pl = _sample_plan(sample_off)
     B = len(so) - 1
-    pl = plan(np.diff(so))
     F, T = int(pl["frame_off"][-1]), int(pl["token_off"][-1])
+    _dev(wave, "wave", torch.float32, numel=int(so[-1]))
     if out is None:
         out = torch.empty((T, model.cfg.out_dim), dtype=torch.float32, device=wave.device)
+    _dev(out, "out", torch.float32, shape=(T, model.cfg.out_dim))
     ws = model.workspace(B, F, T)
     tr = None
     tr_arr = None
@@ -422,9 +476,13 @@ class Resampler:
 def mixdown(x, channels: int, out=None):
     """x: cuda float32 [frames, channels] (or flat, interleaved) -> [frames]."""
     import torch
+    _dev(x, "x", torch.float32)
+    if channels < 1 or x.numel() % channels:
+        raise AeError(AE_ERR_SHAPE, f"x: {x.numel()} values is not whole frames of {channels} channels")
     frames = x.numel() // channels
     if out is None:
         out = torch.empty(frames, dtype=torch.float32, device=x.device)
+    _dev(out, "out", torch.float32, shape=(frames,))
     _check(lib().ae_mixdown(_ptr(x), frames, channels, _ptr(out), _stream()))
     return out
 
@@ -436,8 +494,10 @@ def resample(r: Resampler, x, in_off, out=None):
     io, ip = _i64(in_off)
     B = len(io) - 1
     total = int(r.out_offsets(io)[-1])
+    _dev(x, "x", torch.float32, numel=int(io[-1]))
     if out is None:
         out = torch.empty(total, dtype=torch.float32, device=x.device)
+    _dev(out, "out", torch.float32, shape=(total,))
     ws = r.workspace(B, int(io[-1]), 1, x.device)
     _check(lib().ae_resample(r.handle, _ptr(x), ip, B, _ptr(out), _ptr(ws), ws.numel(),
                              _stream()))
@@ -451,8 +511,10 @@ def to_mono_16k(r: Resampler, x, in_off, channels: int, out=None):
     io, ip = _i64(in_off)
     B = len(io) - 1
     total = int(r.out_offsets(io)[-1])
+    _dev(x, "x", torch.float32, numel=int(io[-1]) * int(channels))
     if out is None:
         out = torch.empty(total, dtype=torch.float32, device=x.device)
+    _dev(out, "out", torch.float32, shape=(total,))
     ws = r.workspace(B, int(io[-1]), channels, x.device)
     _check(lib().ae_to_mono_16k(r.handle, _ptr(x), ip, B, channels, _ptr(out), _ptr(ws),
                                 ws.numel(), _stream()))
@@ -483,7 +545,12 @@ def merge_soft_tokens(ids, x, soft, audio=RELEASE_AUDIO):
     (cuda int32 [L]) take the rows of soft (cuda float32 [S, d]) in order.
     Returns the number of audio rows (a device int64 tensor)."""
     import torch
+    if not torch.is_tensor(x) or x.dim() != 2 or not torch.is_tensor(soft) or soft.dim() != 2:
+        raise AeError(AE_ERR_SHAPE, "x [L, d] and soft [S, d] must be 2-D tensors")
     L, d = x.shape
+    _dev(x, "x", torch.float32)
+    _dev(ids, "ids", torch.int32, shape=(L,))
+    _dev(soft, "soft", torch.float32, shape=(soft.shape[0], d))
     ws = torch.empty(max(int(lib().ae_merge_workspace_bytes(L)), 256), dtype=torch.uint8,
                      device=x.device)
     count = torch.zeros(1, dtype=torch.int64, device=x.device)

@@ -287,7 +287,8 @@ ae_status plan_from_samples(const int64_t* sample_off, int B, Plan& p) {
   if (B < 0) return set_error(AE_ERR_INVALID, "B must be >= 0");
   if (B > 0 && !sample_off) return set_error(AE_ERR_INVALID, "sample_off is NULL");
   p.B = B;
-  p.sample_off.assign(sample_off, sample_off + B + 1);
+  if (sample_off) p.sample_off.assign(sample_off, sample_off + B + 1);
+  else p.sample_off.assign(1, 0);
   if (B > 0 && p.sample_off[0] < 0) return set_error(AE_ERR_INVALID, "sample_off[0] < 0");
   p.frame_off.assign(B + 1, 0);
   for (int i = 0; i < B; ++i) {
@@ -303,7 +304,8 @@ ae_status plan_from_frame_off(const int64_t* frame_off, int B, Plan& p) {
   if (B < 0) return set_error(AE_ERR_INVALID, "B must be >= 0");
   if (B > 0 && !frame_off) return set_error(AE_ERR_INVALID, "frame_off is NULL");
   p.B = B;
-  p.frame_off.assign(frame_off, frame_off + B + 1);
+  if (frame_off) p.frame_off.assign(frame_off, frame_off + B + 1);
+  else p.frame_off.assign(1, 0);
   if (B > 0 && p.frame_off[0] != 0) return set_error(AE_ERR_INVALID, "frame_off[0] must be 0");
   for (int i = 0; i < B; ++i) {
     const int64_t F = p.frame_off[i + 1] - p.frame_off[i];
@@ -617,6 +619,9 @@ ae_status write_tab(const Plan& pl, const Ws& w, hipStream_t s) {
   return AE_OK;
 }
 
+ae_status encode_impl(const ae_model* m, const float* wave, const Plan& pl, float* out,
+                      float* const* trace, const Ws& w, hipStream_t s);
+
 }  // namespace
 
 // ================================================================ C ABI
@@ -661,6 +666,18 @@ ae_status ae_plan(const int64_t* n_samples, int32_t B, int64_t* sample_off, int6
     fo += F;
     ro += T1;
     to += half_up(T1);
+  }
+  return AE_OK;
+}
+
+ae_status ae_plan_frames(const int64_t* frame_off, int32_t B, int64_t* row_off,
+                         int64_t* token_off) {
+  Plan pl;
+  ae_status st = plan_from_frame_off(frame_off, B, pl);
+  if (st != AE_OK) return st;
+  for (int i = 0; i <= B; ++i) {
+    if (row_off) row_off[i] = pl.row_off[i];
+    if (token_off) token_off[i] = pl.token_off[i];
   }
   return AE_OK;
 }
@@ -924,7 +941,18 @@ ae_status ae_encode(const ae_model* m, const float* wave, const int64_t* sample_
   if ((st = check_sizes(m, T, pl.frames())) != AE_OK) return st;
   Ws w = ws_layout(m, B, pl.frames(), T, (char*)ws);
   if ((st = check_ws(ws, ws_bytes, w.total)) != AE_OK) return st;
-  hipStream_t s = (hipStream_t)stream;
+  return encode_impl(m, wave, pl, out, trace, w, (hipStream_t)stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+ae_status encode_impl(const ae_model* m, const float* wave, const Plan& pl, float* out,
+                      float* const* trace, const Ws& w, hipStream_t s) {
+  ae_status st;
+  const int B = pl.B;
+  const int64_t T = pl.tokens();
   AE_HIP_TRY(mel_tables_init());
   if ((st = write_tab(pl, w, s)) != AE_OK) return st;
   AE_LAUNCH(AE_K_LOGMEL, s, launch_logmel(wave, w.tab, w.tab + (B + 1), B, pl.frames(), w.mel, s));
@@ -964,4 +992,4 @@ ae_status ae_encode(const ae_model* m, const float* wave, const int64_t* sample_
   return AE_OK;
 }
 
-}  // extern "C"
+}  // namespace

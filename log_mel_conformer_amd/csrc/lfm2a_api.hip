@@ -381,6 +381,20 @@ ae_status lfm2a_plan(const int64_t* n_samples, int32_t B, int64_t* sample_off,
   return AE_OK;
 }
 
+ae_status lfm2a_plan_frames(const int64_t* frame_off, int32_t B, int64_t* token_off) {
+  if (B < 0 || (B > 0 && !frame_off)) return set_error(AE_ERR_INVALID, "lfm2a_plan_frames: bad batch");
+  if (B > 0 && frame_off[0] != 0) return set_error(AE_ERR_INVALID, "lfm2a_plan_frames: frame_off[0] != 0");
+  int64_t t = 0;
+  if (token_off) token_off[0] = 0;
+  for (int i = 0; i < B; ++i) {
+    const int64_t F = frame_off[i + 1] - frame_off[i];
+    if (F < 0) return set_error(AE_ERR_INVALID, "lfm2a_plan_frames: frame_off must be non-decreasing");
+    t += half_up(half_up(half_up(F)));
+    if (token_off) token_off[i + 1] = t;
+  }
+  return AE_OK;
+}
+
 size_t lfm2a_logmel_workspace_bytes(int32_t B) {
   if (B < 0) return 0;
   return Layout(B, 0, 0, 0, 0, 0).total;

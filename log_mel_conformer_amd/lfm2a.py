@@ -13,7 +13,7 @@ import ctypes as C
 import numpy as np
 
 from . import ae
-from .ae import AeError, _check, _i64, _ptr, _stream
+from .ae import AE_ERR_INVALID, AE_ERR_SHAPE, AeError, _check, _dev, _i64, _ptr, _stream
 
 _P = C.c_void_p
 
@@ -62,6 +62,7 @@ def lib():
             "lfm2a_num_frames": (C.c_int64, [C.c_int64]),
             "lfm2a_num_tokens": (C.c_int64, [C.c_int64]),
             "lfm2a_plan": (C.c_int, [i64p, C.c_int32, i64p, i64p, i64p]),
+            "lfm2a_plan_frames": (C.c_int, [i64p, C.c_int32, i64p]),
             "lfm2a_logmel_workspace_bytes": (C.c_size_t, [C.c_int32]),
             "lfm2a_logmel": (C.c_int, [_P, i64p, C.c_int32, _P, _P, C.c_size_t, _P]),
             "lfm2a_model_create": (C.c_int, [C.POINTER(Config), C.POINTER(Weights), C.c_int, _P,
@@ -110,6 +111,25 @@ def plan(lengths):
     return dict(sample_off=outs[0], frame_off=outs[1], token_off=outs[2])
 
 
+def plan_frames(frame_off):
+    """Token prefix sums of a packed feature layout (host int64 [B+1])."""
+    fo, fp = _i64(frame_off)
+    B = len(fo) - 1
+    to = np.zeros(B + 1, np.int64)
+    _check(lib().lfm2a_plan_frames(fp, B, to.ctypes.data_as(C.POINTER(C.c_int64))))
+    return to
+
+
+def _sample_plan(sample_off):
+    so, sp = _i64(sample_off)
+    if len(so) < 1 or so[0] != 0:
+        raise AeError(AE_ERR_INVALID, "sample_off must start at 0")
+    lens = np.diff(so)
+    if np.any(lens < 0):
+        raise AeError(AE_ERR_INVALID, "sample_off must be non-decreasing")
+    return so, sp, plan(lens)
+
+
 def _ws(nbytes, device="cuda"):
     import torch
     return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
@@ -119,11 +139,13 @@ def logmel(wave, sample_off, out=None):
     """wave: cuda float32 [sum N]; sample_off: host int64 [B+1] ->
     normalised features [sum F, 128]."""
     import torch
-    so, sp = _i64(sample_off)
+    so, sp, pl = _sample_plan(sample_off)
     B = len(so) - 1
-    F = int(sum(num_frames(n) for n in np.diff(so)))
+    F = int(pl["frame_off"][-1])
+    _dev(wave, "wave", torch.float32, numel=int(so[-1]))
     if out is None:
         out = torch.empty((F, 128), dtype=torch.float32, device=wave.device)
+    _dev(out, "out", torch.float32, shape=(F, 128))
     ws = _ws(lib().lfm2a_logmel_workspace_bytes(B), wave.device)
     _check(lib().lfm2a_logmel(_ptr(wave), sp, B, _ptr(out), _ptr(ws), ws.numel(), _stream()))
     return out
@@ -219,24 +241,19 @@ class Model:
             pass
 
 
-def _tokens_of_frames(frames):
-    h = int(frames)
-    for _ in range(3):
-        h = (h - 1) // 2 + 1 if h > 0 else 0
-    return h
-
-
 def stem(model: Model, feat, frame_off, out=None):
     """feat: cuda float32 [sum F, 128]; frame_off: host int64 [B+1] ->
     x [sum T, n_embd] float32."""
     import torch
     fo, fp = _i64(frame_off)
     B = len(fo) - 1
-    toks = [_tokens_of_frames(f) for f in np.diff(fo)]
-    T = int(sum(toks))
+    to = plan_frames(fo)
+    T = int(to[-1])
+    _dev(feat, "feat", torch.float32, numel=int(fo[-1]) * 128)
     if out is None:
         out = torch.empty((T, model.cfg.n_embd), dtype=torch.float32, device=feat.device)
-    ws = model.workspace(B, int(fo[-1]), T, max(toks, default=0))
+    _dev(out, "out", torch.float32, shape=(T, model.cfg.n_embd))
+    ws = model.workspace(B, int(fo[-1]), T, int(np.diff(to).max(initial=0)))
     _check(lib().lfm2a_stem(model.handle, _ptr(feat), fp, B, _ptr(out), _ptr(ws), ws.numel(),
                             _stream()))
     return out
@@ -244,8 +261,10 @@ def stem(model: Model, feat, frame_off, out=None):
 
 def block(model: Model, layer: int, x, token_off):
     """One Conformer block in place on x (cuda float32 [n, n_embd])."""
+    import torch
     to, tp = _i64(token_off)
     B = len(to) - 1
+    _dev(x, "x", torch.float32, shape=(int(to[-1]), model.cfg.n_embd))
     ws = model.workspace(B, 0, int(to[-1]), int(np.diff(to).max(initial=0)))
     _check(lib().lfm2a_block(model.handle, int(layer), _ptr(x), tp, B, _ptr(ws), ws.numel(),
                              _stream()))
@@ -254,9 +273,13 @@ def block(model: Model, layer: int, x, token_off):
 
 def adapter(model: Model, x, out=None):
     import torch
+    if not torch.is_tensor(x) or x.dim() != 2:
+        raise AeError(AE_ERR_SHAPE, "x: a 2-D tensor [n, n_embd] is required")
     n = x.shape[0]
+    _dev(x, "x", torch.float32, shape=(n, model.cfg.n_embd))
     if out is None:
         out = torch.empty((n, model.cfg.llm_hidden), dtype=torch.float32, device=x.device)
+    _dev(out, "out", torch.float32, shape=(n, model.cfg.llm_hidden))
     ws = model.workspace(1, 0, n, 0)
     _check(lib().lfm2a_adapter(model.handle, _ptr(x), n, _ptr(out), _ptr(ws), ws.numel(),
                                _stream()))
@@ -267,15 +290,14 @@ def encode(model: Model, wave, sample_off, out=None):
     """wave: cuda float32 [sum N]; sample_off: host int64 [B+1] ->
     embeddings [sum T, llm_hidden] float32."""
     import torch
-    so, sp = _i64(sample_off)
+    so, sp, pl = _sample_plan(sample_off)
     B = len(so) - 1
-    lens = np.diff(so)
-    F = int(sum(num_frames(n) for n in lens))
-    toks = [num_tokens(n) for n in lens]
-    T = int(sum(toks))
+    F, T = int(pl["frame_off"][-1]), int(pl["token_off"][-1])
+    _dev(wave, "wave", torch.float32, numel=int(so[-1]))
     if out is None:
         out = torch.empty((T, model.cfg.llm_hidden), dtype=torch.float32, device=wave.device)
-    ws = model.workspace(B, F, T, max(toks, default=0))
+    _dev(out, "out", torch.float32, shape=(T, model.cfg.llm_hidden))
+    ws = model.workspace(B, F, T, int(np.diff(pl["token_off"]).max(initial=0)))
     _check(lib().lfm2a_encode(model.handle, _ptr(wave), sp, B, _ptr(out), _ptr(ws), ws.numel(),
                               _stream()))
     return out
@@ -288,8 +310,13 @@ def xl_attention(qkv, p, t_max, u, v, token_off, out=None):
     to, tp = _i64(token_off)
     B = len(to) - 1
     n = int(to[-1])
+    _dev(qkv, "qkv", torch.bfloat16, shape=(n, 1536))
+    _dev(p, "p", torch.bfloat16, shape=(2 * int(t_max) - 1, 512))
+    _dev(u, "u", torch.float32, shape=(512,))
+    _dev(v, "v", torch.float32, shape=(512,))
     if out is None:
         out = torch.empty((n, 512), dtype=torch.bfloat16, device=qkv.device)
+    _dev(out, "out", torch.bfloat16, shape=(n, 512))
     ws = _ws(lib().lfm2a_attention_workspace_bytes(B), qkv.device)
     _check(lib().lfm2a_xl_attention(_ptr(qkv), _ptr(p), int(t_max), _ptr(u), _ptr(v), tp, B,
                                     _ptr(out), _ptr(ws), ws.numel(), _stream()))

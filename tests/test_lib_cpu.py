@@ -158,3 +158,64 @@ def test_expand_ids_refusals():
         ae.expand_ids([A], [98], bos=2, eos=1, max_tokens=100)
     assert e.value.status == ae.AE_ERR_CAPACITY
     assert len(ae.expand_ids([A], [96], bos=2, eos=1, max_tokens=100)) == 100
+
+
+def test_plan_frames_matches_oracle():
+    """ae_plan_frames / lfm2a_plan_frames: conv0-row and token prefix sums
+    from frame offsets, bit-exact with the oracle's counts."""
+    from log_mel_conformer_amd import lfm2a
+    from oracle import lfm2a as olfm
+    lens = [100, 161, 16000, 480000, 0, 72825, 641]
+    fo = np.concatenate([[0], np.cumsum([oracle.num_frames(n) for n in lens])])
+    p = ae.plan_frames(fo)
+    assert np.array_equal(p["token_off"], np.concatenate([[0], np.cumsum([oracle.num_tokens(n) for n in lens])]))
+    assert np.array_equal(p["row_off"], ae.plan(lens)["row_off"])
+    assert np.array_equal(ae.plan_frames([0])["token_off"], [0])
+    for bad in ([1, 5], [0, 5, 3], [0, 3000]):
+        with pytest.raises(ae.AeError):
+            ae.plan_frames(bad)
+    llens = [0, 320, 16000, 480000, 12345]
+    lfo = np.concatenate([[0], np.cumsum([olfm.num_frames(n) for n in llens])])
+    assert np.array_equal(lfm2a.plan_frames(lfo),
+                          np.concatenate([[0], np.cumsum([olfm.num_tokens(n) for n in llens])]))
+    with pytest.raises(ae.AeError):
+        lfm2a.plan_frames([0, 4, 2])
+
+
+def test_binding_refuses_bad_tensors_before_any_call():
+    """Host tensors, the wrong dtype, strided views, short buffers and bad
+    offsets raise AeError in the binding, before the library sees a pointer
+    (a kernel handed any of them would read or write out of bounds)."""
+    import torch
+    from log_mel_conformer_amd import lfm2a
+
+    class _Cfg:
+        hidden, out_dim, n_embd, llm_hidden = 1024, 512, 512, 2048
+
+    class _M:
+        cfg = _Cfg()
+        handle = None
+
+    so = np.array([0, 16000])
+    cases = [
+        lambda: ae.logmel(torch.zeros(16000), so),                               # host tensor
+        lambda: ae.logmel(np.zeros(16000, np.float32), so),                      # not a tensor
+        lambda: ae.logmel(torch.zeros(16000, dtype=torch.float64), so),          # dtype
+        lambda: ae.logmel(torch.zeros(16000), [0, 200, 100]),                    # decreasing
+        lambda: ae.logmel(torch.zeros(16000), [5, 16000]),                       # not from 0
+        lambda: ae.encode(_M(), torch.zeros(16000), so),
+        lambda: ae.subsample(_M(), torch.zeros((99, 128)), [0, 99]),
+        lambda: ae.conformer_layer(_M(), 0, torch.zeros((25, 1024)), torch.zeros(25, dtype=torch.int32)),
+        lambda: ae.conformer_layer(_M(), 0, torch.zeros(25), torch.zeros(25, dtype=torch.int32)),
+        lambda: ae.mixdown(torch.zeros(10), 2),
+        lambda: lfm2a.logmel(torch.zeros(16000), so),
+        lambda: lfm2a.encode(_M(), torch.zeros(16000), so),
+        lambda: lfm2a.adapter(_M(), torch.zeros((4, 512))),
+    ]
+    for i, f in enumerate(cases):
+        with pytest.raises(ae.AeError):
+            f()
+    # the checks themselves: contiguity, size and shape
+    t = torch.zeros((8, 8))
+    with pytest.raises(ae.AeError):
+        ae._dev(t, "t", torch.float32)                    # host tensor refused first
