@@ -215,6 +215,27 @@ ae_status ae_encode(const ae_model* m, const float* wave, const int64_t* sample_
                     int32_t B, float* out, float* const* trace, void* ws, size_t ws_bytes,
                     ae_stream stream);
 
+/* ae_encode without a workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc). Same computation, kernels and results as ae_encode
+ * with trace = NULL; the workspace is instead a static device array of
+ * AE_STATIC_SCRATCH_BYTES per device, which libae.so holds from load until
+ * the process ends. The model, wave, sample_off and out are as for
+ * ae_encode; the current device must be the model's. Allocates nothing: no
+ * hipMalloc, hipFree or allocating library call (the first call on a device
+ * looks up the array's device address once).
+ * Errors: AE_ERR_CAPACITY when the batch needs more than
+ * AE_STATIC_SCRATCH_BYTES (what ae_workspace_bytes reports for it; one 30 s
+ * clip needs about 59 MB in bf16, 110 MB in f32); AE_ERR_INVALID for a
+ * device mismatch or NULL pointers; as ae_encode otherwise.
+ * Calls on one device share the array and the last call's contents stay
+ * in it; every buffer in it is written before it is read within a call, so
+ * nothing needs clearing. Calls that overlap on one device (other streams,
+ * other threads) race on it: serialise them. */
+#define AE_STATIC_SCRATCH_BYTES ((size_t)128 << 20)
+ae_status ae_encode_static(const ae_model* m, const float* wave, const int64_t* sample_off,
+                           int32_t B, float* out, ae_stream stream);
+
 /* --- mixdown and resampling to 16 kHz (ahead of ae_logmel) -------------
  * The page: to_mono_16k, resample_hq and the resampler constants. */
 

@@ -111,6 +111,7 @@ def lib():
             "ae_subsample": (C.c_int, [_P, _P, i64p, C.c_int32, _P, _P, C.c_size_t, _P]),
             "ae_conformer_layer": (C.c_int, [_P, C.c_int32, _P, _P, C.c_int64, _P, C.c_size_t, _P]),
             "ae_encode": (C.c_int, [_P, _P, i64p, C.c_int32, _P, C.POINTER(_P), _P, C.c_size_t, _P]),
+            "ae_encode_static": (C.c_int, [_P, _P, i64p, C.c_int32, _P, _P]),
             "ae_resampled_length": (C.c_int64, [C.c_int64, C.c_int32, C.c_int32]),
             "ae_resampler_create": (C.c_int, [C.c_int32, C.c_int32, _P, C.POINTER(_P)]),
             "ae_resampler_destroy": (None, [_P]),
@@ -418,6 +419,26 @@ def encode(model: Model, wave, sample_off, out=None, trace: bool = False):
                            C.cast(tr_arr, C.POINTER(C.c_void_p)) if tr_arr is not None else None,
                            _ptr(ws), ws.numel(), _stream()))
     return (out, tr) if trace else out
+
+
+STATIC_SCRATCH_BYTES = 128 << 20   # AE_STATIC_SCRATCH_BYTES
+
+
+def encode_static(model: Model, wave, sample_off, out=None):
+    """ae_encode_static: the encoder on the library's static scratch (no
+    workspace; nothing allocated by the call itself). Same results as
+    ``encode``; batches beyond AE_STATIC_SCRATCH_BYTES raise
+    AE_ERR_CAPACITY."""
+    import torch
+    so, sp, pl = _sample_plan(sample_off)
+    B = len(so) - 1
+    T = int(pl["token_off"][-1])
+    _dev(wave, "wave", torch.float32, numel=int(so[-1]))
+    if out is None:
+        out = torch.empty((T, model.cfg.out_dim), dtype=torch.float32, device=wave.device)
+    _dev(out, "out", torch.float32, shape=(T, model.cfg.out_dim))
+    _check(lib().ae_encode_static(model.handle, _ptr(wave), sp, B, _ptr(out), _stream()))
+    return out
 
 
 def resampled_length(n: int, from_rate: int, to_rate: int = 16000) -> int:

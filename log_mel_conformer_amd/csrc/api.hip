@@ -624,6 +624,41 @@ ae_status encode_impl(const ae_model* m, const float* wave, const Plan& pl, floa
 
 }  // namespace
 
+// Scratch memory of ae_encode_static, for callers that cannot allocate: one
+// copy per device, held until the process ends. Host code never passes the
+// array's name to a kernel or a copy (on the host it is only a stand-in
+// symbol); it takes the device address from hipGetSymbolAddress, once per
+// device, and uses that.
+static __device__ __align__(256) unsigned char scratch[AE_STATIC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr size_t kStaticScratchBytes = AE_STATIC_SCRATCH_BYTES;
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+char* g_scratch_ptr[kMaxScratchDevices] = {};
+
+// The device address of `scratch` on device `dev` (the current device).
+ae_status static_scratch(int dev, char** out) {
+  if (dev < 0 || dev >= kMaxScratchDevices)
+    return set_error(AE_ERR_UNSUPPORTED, "device index beyond the static scratch table");
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return set_error(AE_ERR_HIP, std::string("hipGetSymbolAddress(scratch): ") +
+                                       hipGetErrorString(e));
+    if (((uintptr_t)p & 255) != 0)
+      return set_error(AE_ERR_HIP, "static scratch is not 256-byte aligned");
+    g_scratch_ptr[dev] = (char*)p;
+  }
+  *out = g_scratch_ptr[dev];
+  return AE_OK;
+}
+
+}  // namespace
+
 // ================================================================ C ABI
 extern "C" {
 
@@ -942,6 +977,33 @@ ae_status ae_encode(const ae_model* m, const float* wave, const int64_t* sample_
   Ws w = ws_layout(m, B, pl.frames(), T, (char*)ws);
   if ((st = check_ws(ws, ws_bytes, w.total)) != AE_OK) return st;
   return encode_impl(m, wave, pl, out, trace, w, (hipStream_t)stream);
+}
+
+ae_status ae_encode_static(const ae_model* m, const float* wave, const int64_t* sample_off,
+                           int32_t B, float* out, ae_stream stream) {
+  if (!m) return set_error(AE_ERR_INVALID, "model is NULL");
+  Plan pl;
+  ae_status st = plan_from_samples(sample_off, B, pl);
+  if (st != AE_OK) return st;
+  const int64_t T = pl.tokens();
+  if (T == 0) return AE_OK;
+  if (!wave || !out) return set_error(AE_ERR_INVALID, "wave and out must not be NULL");
+  if ((st = check_sizes(m, T, pl.frames())) != AE_OK) return st;
+  const size_t need = ws_layout(m, B, pl.frames(), T, nullptr).total;
+  if (need > kStaticScratchBytes)
+    return set_error(AE_ERR_CAPACITY,
+                     "batch needs " + std::to_string(need) + " bytes of scratch; the static "
+                     "scratch holds " + std::to_string(kStaticScratchBytes) +
+                     " (use ae_encode with a workspace)");
+  int dev = -1;
+  AE_HIP_TRY(hipGetDevice(&dev));
+  if (dev != m->device)
+    return set_error(AE_ERR_INVALID, "the current device (" + std::to_string(dev) +
+                                         ") is not the model's (" + std::to_string(m->device) + ")");
+  char* base = nullptr;
+  if ((st = static_scratch(dev, &base)) != AE_OK) return st;
+  Ws w = ws_layout(m, B, pl.frames(), T, base);
+  return encode_impl(m, wave, pl, out, nullptr, w, (hipStream_t)stream);
 }
 
 }  // extern "C"

@@ -204,6 +204,7 @@ def test_binding_refuses_bad_tensors_before_any_call():
         lambda: ae.logmel(torch.zeros(16000), [0, 200, 100]),                    # decreasing
         lambda: ae.logmel(torch.zeros(16000), [5, 16000]),                       # not from 0
         lambda: ae.encode(_M(), torch.zeros(16000), so),
+        lambda: ae.encode_static(_M(), torch.zeros(16000), so),
         lambda: ae.subsample(_M(), torch.zeros((99, 128)), [0, 99]),
         lambda: ae.conformer_layer(_M(), 0, torch.zeros((25, 1024)), torch.zeros(25, dtype=torch.int32)),
         lambda: ae.conformer_layer(_M(), 0, torch.zeros(25), torch.zeros(25, dtype=torch.int32)),
