@@ -570,13 +570,23 @@ ae_status layer_impl(const ae_model* m, int l, float* h, const int32_t* pos, int
             launch_lconv(dt, w.g, m->dwt + (size_t)l * m->cfg.conv_kernel * d, m->cfg.conv_kernel,
                          L.lc_norm, pos, n, d,
                          L.lc_end_clip.in_lo, L.lc_end_clip.in_hi, w.c, s));
+  // linear_end stores its clamped output; FFN 2's pre-norm row kernel adds
+  // it to h (the light conv's residual has no norm) while the row is in
+  // registers, so the GEMM's epilogue does not wait on reading h
   {
-    GemmParams p = gemm_params(M, d, d, w.c, d, L.lc_end, d, h, d);
+    GemmParams p = gemm_params(M, d, d, w.c, d, L.lc_end, d, w.y, d);
     set_out_clip(p, L.lc_end_clip);
-    AE_LAUNCH(AE_K_GEMM_LCEND, s, launch_gemm(dt, EPI_RESID, A_PLAIN, false, p, s));
+    AE_LAUNCH(AE_K_GEMM_LCEND, s, launch_gemm(dt, EPI_STORE, A_PLAIN, lowp, p, s));
+  }
+  {
+    RowNormParams r = rn_params(n, d, h);
+    r.y = w.y; r.scale = 1.0f;
+    r.w_next = L.ff2_pre; r.n_out = 1; r.a[0] = w.a[0];
+    r.lo[0] = L.ff2_w1_clip.in_lo; r.hi[0] = L.ff2_w1_clip.in_hi;
+    AE_LAUNCH(AE_K_ROWNORM, s, launch_rownorm(dt, r, s));
   }
   // ---- FFN 2
-  st = ffn(L.ff2_pre, L.ff2_w1, L.ff2_w1_clip, L.ff2_w2, L.ff2_w2_clip, false);
+  st = ffn(L.ff2_pre, L.ff2_w1, L.ff2_w1_clip, L.ff2_w2, L.ff2_w2_clip, true);
   if (st != AE_OK) return st;
   {
     RowNormParams r = rn_params(n, d, h);

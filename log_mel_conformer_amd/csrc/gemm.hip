@@ -702,14 +702,15 @@ __global__ void __launch_bounds__(WM * WN * 64, OCC) k_gemm_dl(GemmParams p) {
       soff[i] = __builtin_amdgcn_readfirstlane((uint32_t)((size_t)wrow0 * p.ldb * sizeof(T)));
     }
   }
+  auto issue_one = [&](int i, int buf, int kt) {
+    const int g = wave + i * NW;
+    raw_buffer_load_lds(g * RPG < BM ? rs_a : rs_b,
+                        (__attribute__((address_space(3))) void*)(smem + buf * STAGE + g * 1024),
+                        16, voff[i], soff[i] + (uint32_t)(kt * RB), 0, 0);
+  };
   auto issue = [&](int buf, int kt) {
 #pragma unroll
-    for (int i = 0; i < GPW; ++i) {
-      const int g = wave + i * NW;
-      raw_buffer_load_lds(g * RPG < BM ? rs_a : rs_b,
-                          (__attribute__((address_space(3))) void*)(smem + buf * STAGE + g * 1024),
-                          16, voff[i], soff[i] + (uint32_t)(kt * RB), 0, 0);
-    }
+    for (int i = 0; i < GPW; ++i) issue_one(i, buf, kt);
   };
 
   f32x16 acc[MT][NTL];
@@ -758,8 +759,11 @@ __global__ void __launch_bounds__(WM * WN * 64, OCC) k_gemm_dl(GemmParams p) {
   // A wavefront runs its MFMA run at raised priority, so the SIMD's other
   // wavefront, reading fragments or waiting, does not take issue slots from
   // it (FFN W2 170.1 -> 167.0 us, the LFM2A step 8.16 -> 8.10 ms).
-  auto mfmas = [&](int cur, int nreads, int nloads) {
-    __builtin_amdgcn_s_setprio(1);
+  // s_setprio is a scheduling boundary: a caller that emits fragment reads
+  // or loads to be threaded between the MFMAs raises the priority before
+  // emitting them (raise = false here), or they could not move past it.
+  auto mfmas = [&](int cur, int nreads, int nloads, bool raise = true) {
+    if (raise) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int i = 0; i < MT; ++i)
 #pragma unroll
@@ -799,8 +803,23 @@ __global__ void __launch_bounds__(WM * WN * 64, OCC) k_gemm_dl(GemmParams p) {
         if (kt + STAGES - 1 < nk) wait_vmcnt<GPW * (STAGES - 2)>();
         else wait_vmcnt<0>();
         bare_barrier();
-        issue(kt % STAGES, min(kt + STAGES, nk - 1));
-        mfmas(0, 0, GPW);
+        // the loads one by one between the MFMAs, in program order (the
+        // scheduler, left to itself, bunches them ahead of the MFMAs)
+        __builtin_amdgcn_s_setprio(1);
+        const int rb = kt % STAGES, rk = min(kt + STAGES, nk - 1);
+#pragma unroll
+        for (int q = 0; q < NMFMA; ++q) {
+          Mma<T>::run(acc[q / NTL][q % NTL], fb[0][q % NTL], fa[0][q / NTL]);
+          if (q < GPW) {
+            __builtin_amdgcn_sched_barrier(0);
+            issue_one(q, rb, rk);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+#pragma unroll
+        for (int i = NMFMA; i < GPW; ++i) issue_one(i, rb, rk);
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_setprio(0);
       }
     }
     const unsigned char* sb = smem + ((nk - 1) % STAGES) * STAGE;
@@ -816,6 +835,7 @@ __global__ void __launch_bounds__(WM * WN * 64, OCC) k_gemm_dl(GemmParams p) {
     for (int st = 0; st < NSUB; ++st) {
       const int cur = st & 1;
       if (st + 1 < NSUB) {
+        __builtin_amdgcn_s_setprio(1);
         load_frags(cur ^ 1, sb, st + 1);
       } else {
         // Publish stage kt + 1 (this wave's loads of it have landed and its
@@ -830,12 +850,13 @@ __global__ void __launch_bounds__(WM * WN * 64, OCC) k_gemm_dl(GemmParams p) {
         else wait_vmcnt<0>();
         wait_lgkmcnt0();
         bare_barrier();
+        __builtin_amdgcn_s_setprio(1);
         load_frags(cur ^ 1, smem + ((kt + 1) % STAGES) * STAGE, 0);
         issue(kt % STAGES, min(kt + STAGES, nk - 1));
-        mfmas(cur, NLOAD, GPW);
+        mfmas(cur, NLOAD, GPW, false);
         continue;
       }
-      mfmas(cur, NLOAD, 0);
+      mfmas(cur, NLOAD, 0, false);
     }
   }
   {
@@ -843,8 +864,9 @@ __global__ void __launch_bounds__(WM * WN * 64, OCC) k_gemm_dl(GemmParams p) {
 #pragma unroll
     for (int st = 0; st < NSUB; ++st) {
       const int cur = st & 1;
+      __builtin_amdgcn_s_setprio(1);
       if (st + 1 < NSUB) load_frags(cur ^ 1, sb, st + 1);
-      mfmas(cur, st + 1 < NSUB ? NLOAD : 0, 0);
+      mfmas(cur, st + 1 < NSUB ? NLOAD : 0, 0, false);
     }
   }
   }

@@ -70,7 +70,8 @@ hipError_t launch_conv0_pack(const float* w0, void* frag, hipStream_t s);
 
 // -------------------------------------------------------------- row norms
 // For each row of h [n][d] (float):
-//   if y:     h += scale * rms(y) * w_post   (y [n][d] in dtype dt)
+//   if y:     h += scale * rms(y) * w_post   (y [n][d] in dtype dt), or
+//             h += scale * y when w_post is null
 //   if w_out: h  = rms(h) * w_out
 //   store h (when y or w_out was applied); if h_copy: also h as dtype dt
 //   if w_next: a_i = clamp(rms(h) * w_next, lo_i, hi_i) for i < n_out (dtype dt)

@@ -46,7 +46,17 @@ __global__ void __launch_bounds__(256) k_rownorm(RowNormParams p) {
     const float4 v = *(const float4*)(hrow + q * 256 + lane * 4);
     x[4 * q] = v.x; x[4 * q + 1] = v.y; x[4 * q + 2] = v.z; x[4 * q + 3] = v.w;
   }
-  if (p.y) {
+  if (p.y && !p.w_post) {
+    // a plain residual add (the light conv's linear_end output)
+    const T* yrow = (const T*)p.y + row * d;
+#pragma unroll
+    for (int q = 0; q < NV; ++q) {
+      float y[4];
+      load4(yrow + q * 256 + lane * 4, y);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[4 * q + e] += p.scale * y[e];
+    }
+  } else if (p.y) {
     float y[VPL];
     const T* yrow = (const T*)p.y + row * d;
     float ss = 0.f;
