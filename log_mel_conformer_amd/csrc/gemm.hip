@@ -896,9 +896,24 @@ hipError_t run(const GemmParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
-// fp32 operands (the parity path): register-staged 128x128 tiles.
+// fp32 operands (the parity path): register-staged 128x128 tiles, or for
+// fewer than 4096 rows (a 30 s clip has 750 tokens, where 128x128 tiles
+// give a 1024-column output 48 blocks for 256 CUs) 64x64 tiles of four
+// 32x32 wavefronts (64x128 for the GLU, whose column pairs need 64-column
+// wavefront tiles).
 hipError_t dispatch_f32(int epi, int aload, const GemmParams& p, hipStream_t s) {
   if (aload == A_CONV1) return run<float, float, 128, 32, 4, 1, A_CONV1, EPI_LNRELU>(p, s);
+  if (p.M < 4096) {
+    switch (epi) {
+      case EPI_STORE: return run<float, float, 64, 64, 2, 2, A_PLAIN, EPI_STORE>(p, s);
+      case EPI_SILU: return run<float, float, 64, 64, 2, 2, A_PLAIN, EPI_SILU>(p, s);
+      case EPI_GLU: return run<float, float, 64, 128, 2, 2, A_PLAIN, EPI_GLU>(p, s);
+      case EPI_RESID: return run<float, float, 64, 64, 2, 2, A_PLAIN, EPI_RESID>(p, s);
+      case EPI_BIAS: return run<float, float, 64, 64, 2, 2, A_PLAIN, EPI_BIAS>(p, s);
+      case EPI_ACT: return run<float, float, 64, 64, 2, 2, A_PLAIN, EPI_ACT>(p, s);
+    }
+    return hipErrorInvalidValue;
+  }
   switch (epi) {
     case EPI_STORE: return run<float, float, 128, 128, 2, 2, A_PLAIN, EPI_STORE>(p, s);
     case EPI_SILU: return run<float, float, 128, 128, 2, 2, A_PLAIN, EPI_SILU>(p, s);

@@ -6,26 +6,30 @@
 // FFT is a 256-point complex FFT of z[n] = x[2n] + i x[2n+1] (the last 96
 // z are zero: the frame is 320 samples), split as 256 = 16 x 16: lane j
 // first takes the 16-point DFT over z[16 m + j] in registers (ten nonzero
-// inputs), multiplies by e^{-2 pi i j k / 256}, and the wavefront
-// transposes through LDS; lane j then takes the 16-point DFT over the other
-// index and holds Z[j + 16 k]. The real spectrum follows from
-// 2 X[k] = (Z[k] + conj Z[256-k]) - i e^{-2 pi i k / 512} (Z[k] - conj Z[256-k])
-// (the partner read from LDS); the factor 2 is taken out of the mel
-// weights, which are halved on the host (exact). The mel bank has at most
-// two nonzero weights per bin (506 in all), so each band is a short
-// contiguous dot product over its own bins; lane j takes bands j, j + 16,
-// ..., so the i-th band of every lane comes from the same group of sixteen,
-// and each group reads a fixed number of bins (its widest band's count,
-// the others' weight lists padded with zeros): the loop counts are uniform
-// across the wavefront. All exchanges stay inside a wavefront.
+// inputs), multiplies by e^{-2 pi i j k / 256} (the lane's 15 twiddles kept
+// in registers), and the wavefront transposes through LDS; lane j then
+// takes the 16-point DFT over the other index and holds Z[j + 16 k]. The
+// real spectrum follows from pairs (k, 256 - k):
+// 2 X[k] = 2E + w 2O and 2 X[256-k] = conj(2E - w 2O), with
+// 2E = Z[k] + conj Z[256-k], 2O = -i (Z[k] - conj Z[256-k]) and
+// w = e^{-2 pi i k / 512}; the partner Z[256-k] comes from lane
+// (16 - j) mod 16 by ds_bpermute, so one pair gives two bins. The factor 2
+// is taken out of the mel weights, which are halved on the host (exact).
+// The mel bank has at most two nonzero weights per bin (506 in all), so
+// each band is a short contiguous dot product over its own bins; lane j
+// takes bands j, j + 16, ..., and each group of sixteen bands reads a
+// fixed, compile-time number of bins (its widest band's count, the others'
+// weights padded with zeros). All exchanges stay inside a wavefront.
 //
-// Instruction economy (the kernel is VALU-bound): a frame's samples are
-// read through one pointer with immediate offsets (only a clip's first
-// frame, which starts before the clip, takes a checked path), the lane's
-// window weights stay in registers, and the square root and logarithm are
-// the hardware ones (v_sqrt_f32, v_log_f32: about one ulp, far inside the
-// front end's 1e-4 tolerance). Window, twiddle and band tables are
-// computed on the host in double, rounded to float once, and staged in LDS.
+// Instruction economy (the kernel is bound by VALU issue): a block walks a
+// contiguous run of frames, so a lane finds its clip by one binary search
+// and then only steps forward; a frame's samples are read through one
+// pointer with immediate offsets (only a clip's first frame, which starts
+// before the clip, takes a checked path); the window weights and twiddles
+// stay in registers; the square root and logarithm are the hardware ones
+// (v_sqrt_f32, v_log_f32: about one ulp, far inside the front end's 1e-4
+// tolerance). Window, twiddle and band tables are computed on the host in
+// double, rounded to float once.
 #include <math.h>
 
 #include <algorithm>
@@ -41,15 +45,22 @@ namespace {
 constexpr int kMaxBandW = 1024;
 constexpr int kGroups = kMels / 16;  // band groups: bands 16 i .. 16 i + 15
 constexpr int FPB = 16;        // frames per block (4 per wavefront)
+// Bins read per band of each group (the group's widest band): fixed by the
+// bank (16 kHz, 512-point FFT, 128 HTK bands, 130 edges over 0..8 kHz) and
+// checked against the bank the host builds, so the band loops unroll. Each
+// band's weights sit in a list of its own, padded to whole float4s.
+constexpr int kGroupLen[kGroups] = {2, 2, 2, 3, 4, 6, 8, 11};
+constexpr int group_stride(int i) { return (kGroupLen[i] + 3) & ~3; }
+constexpr int group_woff(int i) { return i == 0 ? 0 : group_woff(i - 1) + 16 * group_stride(i - 1); }
+static_assert(group_woff(kGroups) <= kMaxBandW, "band weights fit the table");
 
 struct MelTables {
   float hann[kFrame];
   float2 tw256[256];        // exp(-2 pi i m / 256)
   float2 tw512[256];        // exp(-2 pi i m / 512), m < 256
   int band_start[kMels];    // first bin a band reads (its padded list stays below bin 257)
-  int group_len[kGroups];   // bins read per band of the group (its widest band's count)
-  int group_woff[kGroups];  // group's weights: [q][16 bands] from here
-  float band_w[kMaxBandW];  // half the filter weights, zero padded
+  float band_w[kMaxBandW];  // half the filter weights: group i, band j of it, bin q at
+                            // group_woff(i) + j * group_stride(i) + q, zero padded
 };
 
 __constant__ MelTables g_mel;
@@ -99,13 +110,11 @@ bool build_tables(MelTables* t) {
   // groups of sixteen bands read a common number of bins; a band whose
   // padded list would run past the last bin starts earlier, its weights
   // shifted to the end of the list
-  int woff = 0;
+  for (int i = 0; i < kMaxBandW; ++i) t->band_w[i] = 0.0f;
   for (int i = 0; i < kGroups; ++i) {
     int q_len = 0;
     for (int j = 0; j < 16; ++j) q_len = std::max(q_len, count[16 * i + j]);
-    if (woff + 16 * q_len > kMaxBandW) return false;
-    t->group_len[i] = q_len;
-    t->group_woff[i] = woff;
+    if (q_len != kGroupLen[i]) return false;  // the kernel's unrolled band loops
     for (int j = 0; j < 16; ++j) {
       const int b = 16 * i + j;
       const int s0 = std::min(start[b], kBins - q_len);
@@ -113,11 +122,10 @@ bool build_tables(MelTables* t) {
       t->band_start[b] = s0;
       for (int q = 0; q < q_len; ++q) {
         const int e = q - shift;
-        t->band_w[woff + 16 * q + j] =
+        t->band_w[group_woff(i) + j * group_stride(i) + q] =
             (e >= 0 && e < count[b]) ? (float)(0.5 * wts[b][e]) : 0.0f;
       }
     }
-    woff += 16 * q_len;
   }
   return true;
 }
@@ -171,6 +179,21 @@ __device__ __forceinline__ void dft16_head10(float2 (&x)[16]) {
   for (int i = 0; i < 16; ++i) x[i] = y[i];
 }
 
+// Per-frame LDS image: the 16x16 transpose (float2, rows padded to 17),
+// later the 257 magnitudes and the 128 outputs at a per-frame offset of
+// 0, 48, 32 or 16 floats (the frame's slot in its wavefront), so the four
+// frames of a wavefront write their magnitudes and outputs into distinct
+// banks.
+__device__ __forceinline__ int mag_off(int f4) { return (64 - 16 * f4) & 63; }
+
+// The partner of lane j's pass-2 bin j + 16 k2 is bin 256 - j - 16 k2,
+// held by lane (16 - j) mod 16 of the same frame in register 15 - k2
+// (lanes 0 and 8 are their own partners; lane 0's partner of k2 sits one
+// register further, in x[(16 - k2) mod 16]).
+__device__ __forceinline__ float bperm(int addr, float v) {
+  return __int_as_float(__builtin_amdgcn_ds_bpermute(addr, __float_as_int(v)));
+}
+
 __global__ void __launch_bounds__(256) k_logmel(const float* __restrict__ wave,
                                                 const int64_t* __restrict__ sample_off,
                                                 const int64_t* __restrict__ frame_off, int B,
@@ -179,10 +202,8 @@ __global__ void __launch_bounds__(256) k_logmel(const float* __restrict__ wave,
   __shared__ float2 tw512[256];
   __shared__ float hann[kFrame];
   __shared__ int bstart[kMels];
-  __shared__ float bw[kMaxBandW];
+  __shared__ __attribute__((aligned(16))) float bw[kMaxBandW];
   __shared__ int64_t soff[MAXB_LDS + 1], foff[MAXB_LDS + 1];
-  // per frame: transpose buffer, then Z in natural order, then magnitudes,
-  // then the 128 outputs
   __shared__ __attribute__((aligned(16))) float2 xbuf[FPB][16 * TLD];
   for (int i = threadIdx.x; i < 256; i += 256) {
     tw256[i] = g_mel.tw256[i];
@@ -200,10 +221,12 @@ __global__ void __launch_bounds__(256) k_logmel(const float* __restrict__ wave,
   __syncthreads();
 
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int fl = wv * 4 + (lane >> 4);   // frame slot in the block
+  const int f4 = lane >> 4;
+  const int fl = wv * 4 + f4;            // frame slot in the block
   const int j = lane & 15;
   float2* T = xbuf[fl];
-  float* M = (float*)xbuf[fl];            // magnitudes, after the split
+  float* M = (float*)xbuf[fl] + mag_off(f4);  // magnitudes, after the split
+  float* O = M + 260;                         // the frame's 128 outputs
   // this lane's samples of a frame are 32 m + 2 j + e (m < 10, e < 2): their
   // window weights, for every frame
   float wj[20];
@@ -211,28 +234,45 @@ __global__ void __launch_bounds__(256) k_logmel(const float* __restrict__ wave,
   for (int m = 0; m < 10; ++m)
 #pragma unroll
     for (int e = 0; e < 2; ++e) wj[2 * m + e] = hann[32 * m + 2 * j + e];
+  // the lane's twiddles: e^{-2 pi i j k1 / 256} between the passes (j k1 <
+  // 256) and e^{-2 pi i (j + 16 k2) / 512} of its split pairs
+  float2 tw1[16], tw2[8];
+#pragma unroll
+  for (int k1 = 1; k1 < 16; ++k1) tw1[k1] = tw256[j * k1];
+#pragma unroll
+  for (int k2 = 0; k2 < 8; ++k2) tw2[k2] = tw512[j + 16 * k2];
+  const int bp_addr = 4 * ((lane & 48) | ((16 - j) & 15));
+  const bool self0 = j == 0;
+  // the lane's mel bands j + 16 i: first bin read
+  int bs[kGroups];
+#pragma unroll
+  for (int i = 0; i < kGroups; ++i) bs[i] = bstart[j + 16 * i];
+  // Each block takes a contiguous run of frames, FPB at a time, so a lane's
+  // clip index only moves forward: a binary search for its first frame,
+  // then a step past any clip that ended since the last group (clips of no
+  // frames are stepped over).
+  const int64_t per = ((total + (int64_t)gridDim.x * FPB - 1) / ((int64_t)gridDim.x * FPB)) * FPB;
+  const int64_t gbeg = (int64_t)blockIdx.x * per;
+  const int64_t gend = gbeg + per < total ? gbeg + per : total;
+  int clip = -1;
+  auto fo = [&](int i) -> int64_t { return lds_off ? foff[i] : frame_off[i]; };
+  auto so = [&](int i) -> int64_t { return lds_off ? soff[i] : sample_off[i]; };
   // Raw samples of the frame group a block handles next: loaded one group
   // ahead (register double buffer). A frame starts 160 samples early; only
   // a clip's first frame reaches before the clip, and it (and a slot past
-  // the last frame) takes the checked path, where samples before the clip
-  // are zeros.
+  // the block's last frame) takes the checked path, where samples before
+  // the clip are zeros.
   float xr[20];
   auto fetch = [&](int64_t g0) {
     const int64_t g = g0 + fl;
     int64_t base = 0;
     int lim = 1 << 30;  // samples below this index are zeros (all, past the end)
-    if (g < total) {
-      int c;
-      int64_t start;
-      if (lds_off) {
-        c = find_clip_lds(foff, B, g);
-        start = soff[c];
-        base = start + (g - foff[c]) * kHop - kHop;
-      } else {
-        c = find_clip(frame_off, B, g);
-        start = sample_off[c];
-        base = start + (g - frame_off[c]) * kHop - kHop;
-      }
+    if (g < gend) {
+      if (clip < 0) clip = lds_off ? find_clip_lds(foff, B, g) : find_clip(frame_off, B, g);
+      else
+        while (fo(clip + 1) <= g) ++clip;
+      const int64_t start = so(clip);
+      base = start + (g - fo(clip)) * kHop - kHop;
       lim = start > base ? (int)(start - base) : 0;
     }
     if (lim == 0) {
@@ -251,75 +291,93 @@ __global__ void __launch_bounds__(256) k_logmel(const float* __restrict__ wave,
         }
     }
   };
-  int64_t g0 = (int64_t)blockIdx.x * FPB;
-  if (g0 < total) fetch(g0);
-  for (; g0 < total; g0 += (int64_t)gridDim.x * FPB) {
+  if (gbeg < gend) fetch(gbeg);
+  for (int64_t g0 = gbeg; g0 < gend; g0 += FPB) {
     const int64_t g = g0 + fl;
-    const bool active = g < total;
+    const bool active = g < gend;
     // pass 1: lane j = n2, DFT over m of z[16 m + j]; z is zero for m >= 10
     float2 x[16];
 #pragma unroll
     for (int m = 0; m < 16; ++m)
       x[m] = m < 10 ? make_float2(xr[2 * m] * wj[2 * m], xr[2 * m + 1] * wj[2 * m + 1])
                     : make_float2(0.f, 0.f);
-    const int64_t g1 = g0 + (int64_t)gridDim.x * FPB;
-    if (g1 < total) fetch(g1);
+    if (g0 + FPB < gend) fetch(g0 + FPB);
     dft16_head10(x);
+    T[j] = x[0];
 #pragma unroll
-    for (int k1 = 0; k1 < 16; ++k1) {
-      const float2 t = k1 == 0 ? x[0] : cmul(x[k1], tw256[(j * k1) & 255]);
-      T[k1 * TLD + j] = t;
-    }
+    for (int k1 = 1; k1 < 16; ++k1) T[k1 * TLD + j] = cmul(x[k1], tw1[k1]);
     wave_sync();
     // pass 2: lane j = k1, DFT over n2
 #pragma unroll
     for (int n2 = 0; n2 < 16; ++n2) x[n2] = T[j * TLD + n2];
     dft16(x);                       // x[k2] = Z[j + 16 k2]
-    wave_sync();
+    // partners Z[256 - j - 16 k2], k2 < 8, from lane (16 - j) mod 16
+    float2 zp[8];
+    {
+      float2 r[8];
 #pragma unroll
-    for (int k2 = 0; k2 < 16; ++k2) T[j + 16 * k2] = x[k2];
-    wave_sync();
-    // real split: twice the magnitudes of bins j + 16 k2 (and 256 on lane 0)
-    float mg[16];
+      for (int k2 = 0; k2 < 8; ++k2)
+        r[k2] = make_float2(bperm(bp_addr, x[15 - k2].x), bperm(bp_addr, x[15 - k2].y));
 #pragma unroll
-    for (int k2 = 0; k2 < 16; ++k2) {
-      const int k = j + 16 * k2;
-      const float2 zk = x[k2], zn = T[(256 - k) & 255];
-      const float ex = zk.x + zn.x, ey = zk.y - zn.y;  // 2 E[k]
-      const float ox = zk.y + zn.y, oy = zn.x - zk.x;  // 2 O[k]
-      const float2 w = tw512[k];
-      const float xx = fmaf(w.x, ox, fmaf(-w.y, oy, ex));
-      const float xy = fmaf(w.x, oy, fmaf(w.y, ox, ey));
-      mg[k2] = __builtin_amdgcn_sqrtf(fmaf(xx, xx, xy * xy));
+      for (int k2 = 0; k2 < 8; ++k2) {
+        const float2 own = k2 == 0 ? x[0] : r[k2 - 1];
+        zp[k2] = make_float2(self0 ? own.x : r[k2].x, self0 ? own.y : r[k2].y);
+      }
     }
-    const float m256 = 2.0f * fabsf(x[0].x - x[0].y);
-    wave_sync();
+    // Real split on pairs (k, 256 - k), k = j + 16 k2: with 2E = Z[k] +
+    // conj Z[256-k] and 2O = -i (Z[k] - conj Z[256-k]), 2 X[k] = 2E + w 2O
+    // and 2 X[256-k] = conj(2E - w 2O), w = e^{-2 pi i k / 512}. Lane 0's
+    // k2 = 0 pair gives X[0] and X[256]; bin 128 (its own partner) is
+    // |2 X[128]| = 2 |Z[128]|, lane 0's x[8]. The factor 2 is taken out of
+    // the mel weights.
+    float mk[8], mn[8];
 #pragma unroll
-    for (int k2 = 0; k2 < 16; ++k2) M[j + 16 * k2] = mg[k2];
-    if (j == 0) M[256] = m256;
+    for (int k2 = 0; k2 < 8; ++k2) {
+      const float2 zk = x[k2], zn = zp[k2];
+      const float ex = zk.x + zn.x, ey = zk.y - zn.y;  // 2E
+      const float ox = zk.y + zn.y, oy = zn.x - zk.x;  // 2O
+      const float2 w = tw2[k2];
+      const float px = fmaf(w.x, ox, -w.y * oy), py = fmaf(w.x, oy, w.y * ox);
+      const float ax = ex + px, ay = ey + py, bx = ex - px, by = ey - py;
+      mk[k2] = __builtin_amdgcn_sqrtf(fmaf(ax, ax, ay * ay));
+      mn[k2] = __builtin_amdgcn_sqrtf(fmaf(bx, bx, by * by));
+    }
+    const float m128 = 2.0f * __builtin_amdgcn_sqrtf(fmaf(x[8].x, x[8].x, x[8].y * x[8].y));
+    wave_sync();  // every lane's pass-2 reads of T are done before M overwrites it
+#pragma unroll
+    for (int k2 = 0; k2 < 8; ++k2) {
+      M[j + 16 * k2] = mk[k2];
+      M[256 - j - 16 * k2] = mn[k2];
+    }
+    if (self0) M[128] = m128;
     wave_sync();
     // mel bands j, j + 16, ..., then the log (v_log_f32 is log2)
     float out[8];
 #pragma unroll
     for (int i = 0; i < kGroups; ++i) {
-      const float* mp = M + bstart[j + 16 * i];
-      const float* wp = bw + g_mel.group_woff[i] + j;
-      const int q_len = g_mel.group_len[i];
+      const float* mp = M + bs[i];
+      const float4* wp = (const float4*)(bw + group_woff(i) + j * group_stride(i));
       float acc = 0.f;
-      for (int q = 0; q < q_len; ++q) acc = fmaf(mp[q], wp[16 * q], acc);
+#pragma unroll
+      for (int q4 = 0; q4 < group_stride(i) / 4; ++q4) {
+        const float4 w = wp[q4];
+        const float wv[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (4 * q4 + e < kGroupLen[i]) acc = fmaf(mp[4 * q4 + e], wv[e], acc);
+      }
       out[i] = __builtin_amdgcn_logf(acc + kMelFloor) * 0.69314718055994530942f;
     }
-    wave_sync();
-    // the frame's 128 outputs through LDS, then 32 contiguous bytes per lane
-    float* O = M + 260;
+    // the frame's 128 outputs through LDS (O does not overlap M), then
+    // 256 contiguous bytes per store instruction of the frame's 16 lanes
 #pragma unroll
     for (int i = 0; i < 8; ++i) O[j + 16 * i] = out[i];
     wave_sync();
     if (active) {
-      const float4 a = *(const float4*)(O + 8 * j), c = *(const float4*)(O + 8 * j + 4);
-      float* dst = mel + g * kMels + 8 * j;
+      const float4 a = *(const float4*)(O + 4 * j), c = *(const float4*)(O + 64 + 4 * j);
+      float* dst = mel + g * kMels + 4 * j;
       *(float4*)dst = a;
-      *(float4*)(dst + 4) = c;
+      *(float4*)(dst + 64) = c;
     }
     wave_sync();
   }
