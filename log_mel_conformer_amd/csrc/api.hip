@@ -153,22 +153,29 @@ __global__ void k_conv1_reorder(const T* __restrict__ w, T* __restrict__ wr) {
 }
 
 // Widening of int8 projections: out[r][c] = bf16(float(q[r][c]) * s[r]),
-// for up to 10 matrices in one launch, 16 values per thread.
+// for up to 10 matrices in one launch. A block covers 4096 consecutive
+// values of one matrix (16 a thread); its matrix comes from the block index
+// through a uniform scan of the prefix of block counts, and each thread's
+// row from one 32-bit division.
 struct DqJobs {
   const int8_t* q[10];
   const float* s[10];
   bf16* out[10];
   int cols[10];
   int64_t first[11];  // prefix of the jobs' 16-value chunk counts
+  int bfirst[11];     // prefix of the jobs' block counts
 };
 
-__global__ void k_dequant(DqJobs j) {
-  const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (g >= j.first[10]) return;
+constexpr int kDqBlockValues = 4096;
+
+__global__ void __launch_bounds__(256) k_dequant(DqJobs j) {
+  const int b = blockIdx.x;
   int k = 0;
-  while (g >= j.first[k + 1]) ++k;
-  const int64_t e = (g - j.first[k]) * 16;
-  const int64_t r = e / j.cols[k];
+  while (b >= j.bfirst[k + 1]) ++k;  // uniform
+  const uint32_t n = (uint32_t)((j.first[k + 1] - j.first[k]) * 16);
+  const uint32_t e = (uint32_t)(b - j.bfirst[k]) * kDqBlockValues + threadIdx.x * 16u;
+  if (e >= n) return;
+  const uint32_t r = e / (uint32_t)j.cols[k];
   const float sc = j.s[k][r];
   const int4 v = *(const int4*)(j.q[k] + e);
   const int words[4] = {v.x, v.y, v.z, v.w};
@@ -196,9 +203,16 @@ hipError_t launch_transpose_taps(const float* w, int d, int K, float* wt, hipStr
   return hipGetLastError();
 }
 
-hipError_t launch_dequant(const DqJobs& j, hipStream_t s) {
-  if (j.first[10] == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_dequant, dim3((unsigned)((j.first[10] + 255) / 256)), dim3(256), 0, s, j);
+hipError_t launch_dequant(const DqJobs& jobs, hipStream_t s) {
+  if (jobs.first[10] == 0) return hipSuccess;
+  DqJobs j = jobs;
+  j.bfirst[0] = 0;
+  for (int k = 0; k < 10; ++k) {
+    const int64_t vals = (j.first[k + 1] - j.first[k]) * 16;
+    if (vals > (int64_t)UINT32_MAX) return hipErrorInvalidValue;
+    j.bfirst[k + 1] = j.bfirst[k] + (int)((vals + kDqBlockValues - 1) / kDqBlockValues);
+  }
+  hipLaunchKernelGGL(k_dequant, dim3((unsigned)j.bfirst[10]), dim3(256), 0, s, j);
   return hipGetLastError();
 }
 

@@ -332,6 +332,23 @@ def test_encode_batch32_bf16_sampled():
         bf16_gate(out[i * 750:(i + 1) * 750], want, f"clip {i}")
 
 
+def test_encode_batch256_bf16_sampled():
+    """256 clips x 30 s through the whole bf16 encoder in one call: 192,000
+    tokens, eight times the benchmark's rows (every projection's M, the
+    conv0 plane of 384,256 rows, offsets past 2^17 rows). The first, a
+    middle and the last clip against the oracle."""
+    say("[gpu] encode: 256 x 30 s white noise, bf16, 192000 tokens, clips 0, 128, 255 vs oracle")
+    W = weights(12, bf16=True)
+    m = ae.Model(W, dtype="bf16")
+    clips = synth.white_batch(256)
+    wave, so = synth.pack(clips)
+    out = ae.encode(m, cuda(wave), so).cpu().numpy()
+    assert out.shape == (256 * 750, 512)
+    assert np.all(np.isfinite(out))
+    for i in (0, 128, 255):
+        bf16_gate(out[i * 750:(i + 1) * 750], oracle.encode_clips([clips[i]], W)[0], f"clip {i}")
+
+
 def test_encode_ragged64_bf16_sampled():
     say("[gpu] encode: 64 ragged pink-noise clips, bf16, 8 clips (shortest, longest, last) vs oracle")
     W = weights(12, bf16=True)
