@@ -394,10 +394,17 @@ ENCODER_NAMES = {
 }
 
 
-def encoder_work(pl, cfg, es, layers, q8=False):
+def encoder_work(pl, cfg, es, layers, q8=False, head=True):
     """Algorithmic work per step of each kernel class of ae_encode: (bound,
-    amount, unit) with flops for the matrix-core classes and bytes for the
-    memory-bound ones. es = bytes per stored activation (2 bf16, 4 fp32)."""
+    amount) with flops for the matrix-core classes and bytes for the
+    memory-bound ones. es = bytes per stored activation (2 bf16, 4 fp32).
+    Row kernels per layer: four launches that read a GEMM output y and h
+    and write h and the next normed input (after FFN 1, after attention,
+    the light conv's residual add with FFN 2's pre-norm, after FFN 2 with
+    norm_out); the first layer's FFN 1 pre-norm reads h and writes its
+    input; the last launch writes the head's bf16 copy of h instead of a
+    next input (nothing in fp32); the head's norm reads and writes 1536
+    columns."""
     T = float(pl["token_off"][-1])
     F = float(pl["frame_off"][-1])
     T1 = float(pl["row_off"][-1])
@@ -406,8 +413,8 @@ def encoder_work(pl, cfg, es, layers, q8=False):
     L = layers
     post = (es + 8 + es) * d           # y in, h read and written, next input out
     pre = (4 + es) * d                  # h in, normed input out
-    last = (es + 8 + (es if es == 2 else 0)) * d
-    rows = pre + L * (3 * post + pre) - post + last + (4 + es) * oh
+    last = (es + 8 + (es if es == 2 and head else 0)) * d
+    rows = pre + L * 4 * post - post + last + ((4 + es) * oh if head else 0)
     w = {
         "logmel": ("hbm", 4.0 * S + 4.0 * 128 * F),
         "conv0": ("hbm", 4.0 * 128 * F + es * T1 * 64 * 128),
@@ -418,7 +425,8 @@ def encoder_work(pl, cfg, es, layers, q8=False):
         "gemm_post": ("mfma", L * 2.0 * T * d * d),
         "gemm_lcstart": ("mfma", L * 2.0 * T * 2 * d * d),
         "gemm_lcend": ("mfma", L * 2.0 * T * d * d),
-        "gemm_head": ("mfma", 2.0 * T * d * 1024 + 2.0 * T * oh * d + 2.0 * T * od * oh),
+        "gemm_head": ("mfma", 2.0 * T * d * 1024 + (2.0 * T * oh * d + 2.0 * T * od * oh
+                                                    if head else 0.0)),
         "rownorm": ("hbm", T * rows),
         "attn": ("hbm", L * T * 4 * es * d),
         "lconv": ("hbm", L * T * 2 * es * d),
@@ -546,10 +554,7 @@ def main():
                 ae.logmel(wave, so, out=mel)
                 ae.subsample(model, mel, pl["frame_off"], out=h)
                 ae.conformer_layer(model, 0, h, pos)
-            work = encoder_work(pl, model.cfg, 4, 1)
-            work.pop("gemm_head")
-            work["rownorm"] = ("hbm", tokens * ((4 + 4) * 1024 + 3 * (4 + 8 + 4) * 1024
-                                                + (4 + 4) * 1024 + (4 + 8) * 1024))
+            work = encoder_work(pl, model.cfg, 4, 1, head=False)
         else:
             out = torch.empty((tokens, 512), dtype=torch.float32, device="cuda")
             step = lambda: ae.encode(model, wave, so, out=out)  # noqa: E731

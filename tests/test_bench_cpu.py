@@ -70,3 +70,34 @@ def test_committed_records_name_their_kernel():
         rec = json.loads(blocks[-1].split("```")[0])
         assert n == f"traffic_{rec['kernel_class']}_{rec['workload']}.md"
         assert rec["hbm_bytes_per_launch"] > 0 and len(rec["sources_sha256"]) == 64
+
+
+def test_encoder_work_matches_independent_counts():
+    """The per-kernel work of the 32 x 30 s step: the projection GEMMs and
+    conv1 total 588.0 MFLOP per token (48.23 per layer x 12, in_proj 2.10,
+    out_proj 3.15, embed 1.57, conv1 2 (32 T) 32 1152 / T = 2.36), 1.411e13
+    FLOP for 24000 tokens; the row kernels' bytes from a per-launch count of
+    what each one reads and writes."""
+    cfg = types.SimpleNamespace(hidden=1024, ff=4096, out_hidden=1536, out_dim=512)
+    T, F, T1, S = 24000, 32 * 2999, 32 * 1500, 32 * 480000
+    pl = {"token_off": [0, T], "frame_off": [0, F], "row_off": [0, T1], "sample_off": [0, S]}
+    w = bench.encoder_work(pl, cfg, 2, 12)
+    gemm = sum(v for k, (b, v) in w.items() if k.startswith("gemm_") or k == "conv1")
+    assert abs(gemm / T / 1e6 - 588.0) < 0.05
+    assert abs(gemm / 1e13 - 1.411) < 0.001
+    assert w["conv1"][1] == 2.0 * 32 * T * 32 * 1152
+    # row kernels, launch by launch (bf16 activations, fp32 h, d = 1024)
+    d, es = 1024, 2
+    launches = [(4 + es) * d]                       # layer 0's FFN 1 pre-norm
+    for layer in range(12):
+        launches += [(es + 8 + es) * d] * 3         # post FFN 1, post attention, lc add + FFN 2 pre
+        launches += [(es + 8 + es) * d]             # post FFN 2 + norm_out + next pre / bf16 copy
+    launches[-1] = (es + 8 + es) * d                # the last layer writes the head's bf16 copy
+    # FFN 2's pre-norm of each layer (h in, a out) is inside the lc add launch,
+    # and each layer's first FFN 1 pre-norm after layer 0 is inside the
+    # previous layer's last launch: 49 launches, plus the head's
+    launches.append((4 + es) * 1536)
+    assert len(launches) == 50
+    assert abs(w["rownorm"][1] - T * sum(launches)) < 1.0
+    assert w["logmel"][1] == 4.0 * S + 512.0 * F
+    assert w["attn"][1] == 12 * T * 4 * es * d and w["lconv"][1] == 12 * T * 2 * es * d
