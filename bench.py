@@ -51,7 +51,7 @@ PEAK_F64_TFLOPS = 78.6   # fp64 vector FMA: 256 CUs x 64 lanes x 2 flops x 2.4 G
 # were taken.
 KERNEL_SOURCES = {
     "logmel": ["logmel.hip", "fft16.h", "launch.h", "common.h"],
-    "gemm": ["gemm.hip", "launch.h", "common.h"],
+    "gemm": ["gemm.hip", "lds_dma.h", "launch.h", "common.h"],
     "resample": ["resample.hip", "launch.h", "common.h"],
     "merge": ["placement.hip", "launch.h", "common.h"],
 }

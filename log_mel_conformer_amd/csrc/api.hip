@@ -21,7 +21,7 @@ struct ae_model {
   std::vector<ae_layer_weights> layers;
   int head_dim, left, n_dist;
   float q_scale, k_scale;
-  float* R = nullptr;         // [layers][n_dist][hidden]
+  void* R = nullptr;          // [layers][n_dist][hidden], storage type
   float* colscale = nullptr;  // [layers][3 hidden]
   void* conv1r = nullptr;     // [32][9 * 128], model dtype
   void* conv0f = nullptr;     // bf16 models: conv0's centred taps as matrix-core fragments
@@ -104,9 +104,10 @@ __global__ void k_token_index(const int64_t* token_off, int B, int64_t n, int32_
 
 // R[dist][j] = sum_i PE[dist][i] rel_k[j][i]; PE row dist = [sin(dist inv_i),
 // cos(dist inv_i)], inv_i = exp(-i ln(10000) / (d/2 - 1)). One wavefront per
-// output, double accumulation (a one-off table).
+// output, double accumulation (a one-off table), stored in the model's
+// storage type (bf16 models round it).
 template <typename T>
-__global__ void k_relative_keys(const T* __restrict__ W, int d, int n_dist, float* __restrict__ R) {
+__global__ void k_relative_keys(const T* __restrict__ W, int d, int n_dist, T* __restrict__ R) {
   const int64_t wid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (wid >= (int64_t)n_dist * d) return;
@@ -122,7 +123,7 @@ __global__ void k_relative_keys(const T* __restrict__ W, int d, int n_dist, floa
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
-  if (lane == 0) R[wid] = (float)acc;
+  if (lane == 0) R[wid] = from_f32<T>((float)acc);
 }
 
 // q columns: q_scale * softplus(per_dim_scale[j % head_dim]) (torch's
@@ -236,15 +237,15 @@ hipError_t launch_token_index(const int64_t* token_off, int B, int64_t n, int32_
   return hipGetLastError();
 }
 
-hipError_t launch_relative_keys(ae_dtype dt, const void* rel_k, int d, int n_dist, float* R,
+hipError_t launch_relative_keys(ae_dtype dt, const void* rel_k, int d, int n_dist, void* R,
                                 hipStream_t s) {
   const unsigned grid = (unsigned)(((int64_t)n_dist * d + 3) / 4);
   if (dt == AE_BF16)
     hipLaunchKernelGGL(k_relative_keys<bf16>, dim3(grid), dim3(256), 0, s, (const bf16*)rel_k, d,
-                       n_dist, R);
+                       n_dist, (bf16*)R);
   else
     hipLaunchKernelGGL(k_relative_keys<float>, dim3(grid), dim3(256), 0, s, (const float*)rel_k,
-                       d, n_dist, R);
+                       d, n_dist, (float*)R);
   return hipGetLastError();
 }
 
@@ -477,6 +478,7 @@ ae_status layer_impl(const ae_model* m, int l, float* h, const int32_t* pos, int
   const int M = (int)n;
   const ae_dtype dt = m->dt;
   const bool lowp = dt == AE_BF16;
+  const size_t es = lowp ? 2 : 4;
   if (n == 0) return AE_OK;
   // int8 models: widen this layer's ten projections into the workspace and
   // run the layer on the widened copies
@@ -558,7 +560,7 @@ ae_status layer_impl(const ae_model* m, int l, float* h, const int32_t* pos, int
     AE_LAUNCH(AE_K_GEMM_QKV, s, launch_gemm(dt, EPI_STORE, A_PLAIN, lowp, p, s));
   }
   AE_LAUNCH(AE_K_ATTN, s,
-            launch_attention(dt, w.qkv, m->R + (size_t)l * m->n_dist * d, pos, n, d,
+            launch_attention(dt, w.qkv, (const char*)m->R + es * l * m->n_dist * d, pos, n, d,
                              m->cfg.heads, m->left, m->cfg.softcap, L.post_clip.in_lo,
                              L.post_clip.in_hi, w.o, s));
   {
@@ -872,7 +874,7 @@ static ae_status model_create_impl(const ae_config* cfg, const ae_weights* w, ae
     return set_error(AE_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
   };
   hipError_t e;
-  if ((e = hipMalloc((void**)&m->R, sizeof(float) * (size_t)c.layers * n_dist * c.hidden)) != hipSuccess)
+  if ((e = hipMalloc(&m->R, es * c.layers * n_dist * c.hidden)) != hipSuccess)
     return fail(e, "hipMalloc(R)");
   if ((e = hipMalloc((void**)&m->colscale, sizeof(float) * (size_t)c.layers * 3 * c.hidden)) != hipSuccess)
     return fail(e, "hipMalloc(colscale)");
@@ -883,7 +885,7 @@ static ae_status model_create_impl(const ae_config* cfg, const ae_weights* w, ae
   for (int l = 0; l < c.layers; ++l) {
     const ae_layer_weights& L = m->layers[l];
     if ((e = launch_relative_keys(dt, L.rel_k, c.hidden, n_dist,
-                                  m->R + (size_t)l * n_dist * c.hidden, s)) != hipSuccess)
+                                  (char*)m->R + es * l * n_dist * c.hidden, s)) != hipSuccess)
       return fail(e, "relative keys");
     if ((e = launch_transpose_taps(L.lc_dw, c.hidden, c.conv_kernel,
                                    m->dwt + (size_t)l * c.conv_kernel * c.hidden, s)) != hipSuccess)

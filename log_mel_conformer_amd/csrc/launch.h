@@ -96,7 +96,7 @@ hipError_t launch_rownorm(ae_dtype dt, const RowNormParams& p, hipStream_t s);
 // ------------------------------------------------------------- attention
 // qkv [n][3d] (dtype dt; q, k already scaled), R [left][d] float,
 // pos [n] -> o [n][d] (dtype dt) clamped to [lo, hi].
-hipError_t launch_attention(ae_dtype dt, const void* qkv, const float* R, const int32_t* pos,
+hipError_t launch_attention(ae_dtype dt, const void* qkv, const void* R, const int32_t* pos,
                             int64_t n, int d, int heads, int left, float softcap, float lo,
                             float hi, void* o, hipStream_t s);
 
@@ -115,7 +115,7 @@ hipError_t launch_token_index(const int64_t* token_off, int B, int64_t n_tok, in
                               int32_t* tok_clip, hipStream_t s);
 // Model tables: R = PE rel_k^T ([n_dist][d] float), colscale for q|k|v,
 // conv1 weights reordered to [32][(dt*3+df)*128 + ci].
-hipError_t launch_relative_keys(ae_dtype dt, const void* rel_k, int d, int n_dist, float* R,
+hipError_t launch_relative_keys(ae_dtype dt, const void* rel_k, int d, int n_dist, void* R,
                                 hipStream_t s);
 hipError_t launch_qkv_scale(const float* pds, int d, int head_dim, float q_scale, float k_scale,
                             float* colscale, hipStream_t s);

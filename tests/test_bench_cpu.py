@@ -44,7 +44,7 @@ def _record(tmp_path, kclass, workload, sha, hbm):
 def test_traffic_record_needs_matching_sources(tmp_path, monkeypatch):
     csrc = tmp_path / "log_mel_conformer_amd" / "csrc"
     csrc.mkdir(parents=True)
-    for f in ("gemm.hip", "launch.h", "common.h"):
+    for f in bench.KERNEL_SOURCES["gemm"]:
         (csrc / f).write_text(f"// {f}\n")
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
     sha = bench.sources_sha256("gemm_ffn1")
