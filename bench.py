@@ -431,6 +431,11 @@ def encoder_work(pl, cfg, es, layers, q8=False, head=True):
         "attn": ("hbm", L * T * 4 * es * d),
         "lconv": ("hbm", L * T * 2 * es * d),
     }
+    if es == 2:
+        # bf16 models run both convolutions in one kernel (timed as conv1):
+        # conv0's 64 x 128 x 9 multiply-adds per conv0 row join conv1's
+        del w["conv0"]
+        w["conv1"] = ("mfma", w["conv1"][1] + 2.0 * T1 * 64 * 128 * 9)
     if q8:
         w["dequant"] = ("hbm", L * 3.0 * (2 * ff * d * 2 + 7 * d * d) * 1.0)
     return w

@@ -372,7 +372,8 @@ Ws ws_layout(const ae_model* m, int B, int64_t F, int64_t T, char* base) {
   w.tok_pos = (int32_t*)take(sizeof(int32_t) * (size_t)T);
   w.tok_clip = (int32_t*)take(sizeof(int32_t) * (size_t)T);
   w.mel = (float*)take(sizeof(float) * (size_t)F * kMels);
-  w.y0 = take(es * (size_t)T1 * kF1 * kC0);
+  // the conv0 plane: fp32 models only (bf16 models keep it on chip)
+  w.y0 = m->dt == AE_BF16 ? nullptr : take(es * (size_t)T1 * kF1 * kC0);
   w.x1 = take(es * (size_t)T * kC1 * kF2);
   w.h = (float*)take(sizeof(float) * (size_t)T * d);
   for (int i = 0; i < 3; ++i) w.a[i] = take(es * (size_t)T * d);
@@ -451,17 +452,24 @@ ae_status subsample_impl(const ae_model* m, const float* mel, const Plan& pl, co
   const int64_t T = pl.tokens();
   if (T == 0) return AE_OK;
   AE_HIP_TRY(launch_token_index(d_tok, B, T, w.tok_pos, w.tok_clip, s));
-  AE_LAUNCH(AE_K_CONV0, s, launch_conv0(m->dt, mel, d_frame, d_row, B, pl.rows(), m->w.conv0,
-                                        m->conv0f, m->w.ln0, w.y0, s));
-  GemmParams p = gemm_params((int)(T * 32), kC1, kC0 * 9, nullptr, 0, m->conv1r, kC0 * 9, w.x1,
-                             kC1);
-  p.y0 = w.y0;
-  p.row_off = d_row;
-  p.tok_pos = w.tok_pos;
-  p.tok_clip = w.tok_clip;
-  p.n_tok = (int)T;
-  p.gain = m->w.ln1;
-  AE_LAUNCH(AE_K_CONV1, s, launch_gemm(m->dt, EPI_LNRELU, A_CONV1, true, p, s));
+  if (m->dt == AE_BF16) {
+    // both convolutions in one pass, the conv0 plane kept on chip
+    AE_LAUNCH(AE_K_CONV1, s, launch_subsample_fused(mel, d_frame, d_row, w.tok_pos, w.tok_clip, T,
+                                                    m->conv0f, m->w.ln0, m->conv1r, m->w.ln1,
+                                                    w.x1, s));
+  } else {
+    AE_LAUNCH(AE_K_CONV0, s, launch_conv0(m->dt, mel, d_frame, d_row, B, pl.rows(), m->w.conv0,
+                                          m->w.ln0, w.y0, s));
+    GemmParams p = gemm_params((int)(T * 32), kC1, kC0 * 9, nullptr, 0, m->conv1r, kC0 * 9, w.x1,
+                               kC1);
+    p.y0 = w.y0;
+    p.row_off = d_row;
+    p.tok_pos = w.tok_pos;
+    p.tok_clip = w.tok_clip;
+    p.n_tok = (int)T;
+    p.gain = m->w.ln1;
+    AE_LAUNCH(AE_K_CONV1, s, launch_gemm(m->dt, EPI_LNRELU, A_CONV1, true, p, s));
+  }
   const int d = m->cfg.hidden;
   GemmParams q = gemm_params((int)T, d, kC1 * kF2, w.x1, kC1 * kF2, m->w.in_proj, kC1 * kF2, x, d);
   AE_LAUNCH(AE_K_GEMM_HEAD, s, launch_gemm(m->dt, EPI_STORE, A_PLAIN, false, q, s));

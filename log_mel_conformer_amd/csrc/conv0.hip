@@ -16,19 +16,15 @@
 // channels-last [row][f][c], which is what conv1's implicit GEMM gathers
 // 16-byte chunks from.
 //
-// bf16 storage takes a matrix-core form instead (k_conv0_mfma): the nine
+// bf16 models run both convolutions in one pass (subsample.hip); the
+// matrix-core fragments of their centred taps are packed here: the nine
 // taps of a position against 128 channels are a 32 x 128 x 9 contraction,
-// run as v_mfma_f32_32x32x16_bf16 with every operand split into bf16
-// high and low parts (the three cross terms hi.hi + hi.lo + lo.hi, 27 of
-// the 32 k slots, about 2^-16 relative: far below the bf16 rounding of
-// the output). The taps are centred first (each tap minus its mean over
-// the channels), so the products are already the channel-centred values
-// the LayerNorm needs: the mean pass disappears and the norm is the
-// variance, one 64-value sum and a swap between the two half-waves. Each
-// wavefront owns one output row at a time (64 positions, two 32-position
-// tiles), its three log-mel rows and a staging slice in LDS: outputs go
-// through LDS so that every store instruction writes 1 KB of contiguous
-// rows, and no block-wide barrier is needed after the gains are staged.
+// run as v_mfma_f32_32x32x16_bf16 with every operand split into bf16 high
+// and low parts (the three cross terms hi.hi + hi.lo + lo.hi, 27 of the 32
+// k slots, about 2^-16 relative: far below the bf16 rounding of the
+// output). The taps are centred first (each tap minus its mean over the
+// channels), so the products are already the channel-centred values the
+// LayerNorm needs: the mean pass disappears and the norm is the variance.
 #include "launch.h"
 
 namespace ae {
@@ -40,7 +36,6 @@ constexpr int kConv0Rows = 8;  // output rows per block
 // every cache: its stores are non-temporal (they skip cache allocation;
 // measured 239 -> 175 us for the 786 MB bf16 plane, and conv1 reading it
 // 293 -> 269 us).
-typedef unsigned int u32v4 __attribute__((ext_vector_type(4)));
 typedef float f32v4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ void store8(float* p, const float* v) {
   __builtin_nontemporal_store(f32v4{v[0], v[1], v[2], v[3]}, (f32v4*)p);
@@ -153,120 +148,6 @@ __global__ void k_conv0_pack(const float* __restrict__ w0, uint4* __restrict__ f
   }
 }
 
-constexpr int kMfRows = 8;      // output rows per block, two per wavefront
-constexpr int kStPitch = 136;   // bf16 per staged position (272 bytes: spreads banks)
-
-__global__ void __launch_bounds__(256) k_conv0_mfma(const float* __restrict__ mel,
-                                                    const int64_t* __restrict__ frame_off,
-                                                    const int64_t* __restrict__ row_off, int B,
-                                                    int64_t total_rows,
-                                                    const uint4* __restrict__ frag,
-                                                    const float* __restrict__ g0,
-                                                    bf16* __restrict__ y0) {
-  __shared__ __attribute__((aligned(16))) float gs[kC0];
-  __shared__ float mrow[4][3][kMels + 2];
-  __shared__ __attribute__((aligned(16))) bf16 st[4][32 * kStPitch];
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int p = lane & 31, h = lane >> 5;
-  for (int i = threadIdx.x; i < kC0; i += 256) gs[i] = g0[i];
-  // this lane's first-operand fragments: 4 channel tiles x 2 k-steps
-  uint4 wf[4][2];
-#pragma unroll
-  for (int ct = 0; ct < 4; ++ct)
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) wf[ct][ks] = frag[(ct * 2 + ks) * 64 + lane];
-  __syncthreads();
-  float* m = &mrow[w][0][0];
-  bf16* sw = st[w];
-  for (int rr = w; rr < kMfRows; rr += 4) {
-    const int64_t r = (int64_t)blockIdx.x * kMfRows + rr;
-    if (r >= total_rows) break;  // uniform per wavefront
-    const int c = find_clip(row_off, B, r);
-    const int t1 = (int)(r - row_off[c]);
-    const int64_t fbase = frame_off[c];
-    const int F = (int)(frame_off[c + 1] - fbase);
-    // the row's three log-mel rows 2 t1 - 1 .. 2 t1 + 1 with a zero border
-    for (int idx = lane; idx < 3 * (kMels + 2); idx += 64) {
-      const int dt = idx / (kMels + 2), j = idx - dt * (kMels + 2);
-      const int ti = 2 * t1 + dt - 1, fi = j - 1;
-      float v = 0.f;
-      if (ti >= 0 && ti < F && fi >= 0 && fi < kMels) v = mel[(fbase + ti) * kMels + fi];
-      m[idx] = v;
-    }
-    wave_sync();
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const int f = half * 32 + p;
-      // the position's nine inputs, split into bf16 high and low parts
-      bf16 ph[9], pl[9];
-#pragma unroll
-      for (int dt = 0; dt < 3; ++dt)
-#pragma unroll
-        for (int df = 0; df < 3; ++df) {
-          const float x = m[dt * (kMels + 2) + 2 * f + df];  // column 2f + df - 1, shifted
-          const bf16 hi = (bf16)x;
-          ph[dt * 3 + df] = hi;
-          pl[dt * 3 + df] = (bf16)(x - (float)hi);
-        }
-      auto slot = [&](int k) -> bf16 {
-        if (k >= 27) return (bf16)0.f;
-        const int term = k / 9, tap = k - 9 * term;
-        return term == 1 ? pl[tap] : ph[tap];
-      };
-      bf16x8 a0, a1, b0, b1;  // k-step 0 / 1 for half-wave 0 / 1
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        a0[i] = slot(i);
-        b0[i] = slot(8 + i);
-        a1[i] = slot(16 + i);
-        b1[i] = slot(24 + i);
-      }
-      const bf16x8 x0 = h ? b0 : a0, x1 = h ? b1 : a1;
-      f32x16 acc[4];
-#pragma unroll
-      for (int ct = 0; ct < 4; ++ct) {
-#pragma unroll
-        for (int v = 0; v < 16; ++v) acc[ct][v] = 0.f;
-        acc[ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, wf[ct][0]), x0,
-                                                          acc[ct], 0, 0, 0);
-        acc[ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, wf[ct][1]), x1,
-                                                          acc[ct], 0, 0, 0);
-      }
-      // acc[ct][v] = centred output of channel 32 ct + 8 (v / 4) + 4 h + v % 4
-      float q = 0.f;
-#pragma unroll
-      for (int ct = 0; ct < 4; ++ct)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) q += acc[ct][v] * acc[ct][v];
-      q += __shfl_xor(q, 32, 64);
-      const float inv = rsqrtf(q * (1.0f / kC0) + kEps);
-#pragma unroll
-      for (int ct = 0; ct < 4; ++ct)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int ch = ct * 32 + j * 8 + h * 4;
-          const float4 g = *(const float4*)&gs[ch];
-          typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-          const bf16x4 o = {(bf16)fmaxf(acc[ct][4 * j] * inv * g.x, 0.f),
-                            (bf16)fmaxf(acc[ct][4 * j + 1] * inv * g.y, 0.f),
-                            (bf16)fmaxf(acc[ct][4 * j + 2] * inv * g.z, 0.f),
-                            (bf16)fmaxf(acc[ct][4 * j + 3] * inv * g.w, 0.f)};
-          *(bf16x4*)&sw[p * kStPitch + ch] = o;
-        }
-      wave_sync();
-      // 32 positions x 256 bytes, written as 4 whole positions per instruction
-      bf16* dst = y0 + ((size_t)r * kF1 + half * 32) * kC0;
-#pragma unroll
-      for (int it = 0; it < 8; ++it) {
-        const int pp = it * 4 + (lane >> 4), q16 = lane & 15;
-        __builtin_nontemporal_store(*(const u32v4*)&sw[pp * kStPitch + q16 * 8],
-                                    (u32v4*)(dst + (size_t)pp * kC0 + q16 * 8));
-      }
-      wave_sync();
-    }
-  }
-}
-
 }  // namespace
 
 hipError_t launch_conv0_pack(const float* w0, void* frag, hipStream_t s) {
@@ -276,18 +157,12 @@ hipError_t launch_conv0_pack(const float* w0, void* frag, hipStream_t s) {
 
 hipError_t launch_conv0(ae_dtype dt, const float* mel, const int64_t* frame_off,
                         const int64_t* row_off, int B, int64_t total_rows, const float* w0,
-                        const void* w0_frag, const float* g0, void* y0, hipStream_t s) {
+                        const float* g0, void* y0, hipStream_t s) {
   if (total_rows <= 0) return hipSuccess;
-  if (dt == AE_BF16) {
-    if (!w0_frag) return hipErrorInvalidValue;
-    const unsigned grid = (unsigned)((total_rows + kMfRows - 1) / kMfRows);
-    hipLaunchKernelGGL(k_conv0_mfma, dim3(grid), dim3(256), 0, s, mel, frame_off, row_off, B,
-                       total_rows, (const uint4*)w0_frag, g0, (bf16*)y0);
-  } else {
-    const unsigned grid = (unsigned)((total_rows + kConv0Rows - 1) / kConv0Rows);
-    hipLaunchKernelGGL(k_conv0<float>, dim3(grid), dim3(256), 0, s, mel, frame_off, row_off, B,
-                       total_rows, w0, g0, (float*)y0);
-  }
+  if (dt == AE_BF16) return hipErrorInvalidValue;  // bf16: launch_subsample_fused
+  const unsigned grid = (unsigned)((total_rows + kConv0Rows - 1) / kConv0Rows);
+  hipLaunchKernelGGL(k_conv0<float>, dim3(grid), dim3(256), 0, s, mel, frame_off, row_off, B,
+                     total_rows, w0, g0, (float*)y0);
   return hipGetLastError();
 }
 

@@ -940,10 +940,7 @@ hipError_t run_bf16(const GemmParams& p, hipStream_t s) {
 }
 
 hipError_t dispatch_bf16(int epi, int aload, bool out_bf16, const GemmParams& p, hipStream_t s) {
-  if (aload == A_CONV1) {
-    if (out_bf16) return run<bf16, bf16, 128, 32, 4, 1, A_CONV1, EPI_LNRELU>(p, s);
-    return run<bf16, float, 128, 32, 4, 1, A_CONV1, EPI_LNRELU>(p, s);
-  }
+  if (aload == A_CONV1) return hipErrorInvalidValue;  // bf16: launch_subsample_fused
   if (p.N % 128 != 0) return hipErrorInvalidValue;
   switch (epi) {
     case EPI_STORE:

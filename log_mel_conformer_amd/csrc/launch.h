@@ -60,13 +60,25 @@ hipError_t launch_logmel(const float* wave, const int64_t* sample_off, const int
                          int B, int64_t total_frames, float* mel, hipStream_t s);
 
 // --------------------------------------------------------------- conv0
-// w0_frag: the bf16 path's matrix-core fragments of the centred taps
-// (launch_conv0_pack, 8 KB); unused for float storage.
+// float storage only (bf16 models run launch_subsample_fused); the packed
+// fragments of the centred taps (8 KB) are the fused subsampler's.
 hipError_t launch_conv0(ae_dtype dt, const float* mel, const int64_t* frame_off,
                         const int64_t* row_off, int B, int64_t total_rows, const float* w0,
-                        const void* w0_frag, const float* g0, void* y0, hipStream_t s);
+                        const float* g0, void* y0, hipStream_t s);
 constexpr size_t kConv0FragBytes = 4 * 2 * 64 * 16;
 hipError_t launch_conv0_pack(const float* w0, void* frag, hipStream_t s);
+
+// ------------------------------------------------- subsampler, bf16 models
+// conv0 and conv1 (with their LayerNorms and ReLUs) in one pass, the conv0
+// plane kept in LDS: mel [frames][128] float, the per-clip frame and conv0
+// row offsets, each token's position and clip, the packed conv0 taps
+// (launch_conv0_pack), g0 [128], w1 conv1's weights [32][9 * 128] bf16,
+// g1 [32]; x1 [n_tok][32 * 32] bf16, [frequency][channel] per token.
+hipError_t launch_subsample_fused(const float* mel, const int64_t* frame_off,
+                                  const int64_t* row_off, const int32_t* tok_pos,
+                                  const int32_t* tok_clip, int64_t n_tok, const void* w0_frag,
+                                  const float* g0, const void* w1, const float* g1, void* x1,
+                                  hipStream_t s);
 
 // -------------------------------------------------------------- row norms
 // For each row of h [n][d] (float):

@@ -82,10 +82,15 @@ def test_encoder_work_matches_independent_counts():
     T, F, T1, S = 24000, 32 * 2999, 32 * 1500, 32 * 480000
     pl = {"token_off": [0, T], "frame_off": [0, F], "row_off": [0, T1], "sample_off": [0, S]}
     w = bench.encoder_work(pl, cfg, 2, 12)
-    gemm = sum(v for k, (b, v) in w.items() if k.startswith("gemm_") or k == "conv1")
+    # bf16: the conv1 class is the fused subsampler, conv0's flops included
+    conv0 = 2.0 * T1 * 64 * 128 * 9
+    assert "conv0" not in w and w["conv1"][1] == 2.0 * 32 * T * 32 * 1152 + conv0
+    gemm = sum(v for k, (b, v) in w.items() if k.startswith("gemm_") or k == "conv1") - conv0
     assert abs(gemm / T / 1e6 - 588.0) < 0.05
     assert abs(gemm / 1e13 - 1.411) < 0.001
-    assert w["conv1"][1] == 2.0 * 32 * T * 32 * 1152
+    wf = bench.encoder_work(pl, cfg, 4, 12)
+    assert wf["conv1"][1] == 2.0 * 32 * T * 32 * 1152
+    assert wf["conv0"][1] == 4.0 * 128 * F + 4 * T1 * 64 * 128
     # row kernels, launch by launch (bf16 activations, fp32 h, d = 1024)
     d, es = 1024, 2
     launches = [(4 + es) * d]                       # layer 0's FFN 1 pre-norm
