@@ -179,6 +179,31 @@ def test_subsample_ragged_bf16():
     assert off == g.shape[0]
 
 
+def test_subsample_many_short_clips_bf16():
+    """The bf16 subsampler walks runs of consecutive tokens (about
+    tokens / 512 a block) with a three-row window of conv0 rows: 400 clips
+    of 1-200 frames (about 10^4 tokens, runs of about 20 tokens, most of
+    them crossing clip boundaries), each clip against the oracle."""
+    say("[gpu] subsample: 400 clips of 1-200 frames, bf16")
+    W = weights(1, bf16=True)
+    m = ae.Model(W, dtype="bf16")
+    rng = np.random.default_rng(400)
+    Fs = [int(f) for f in rng.integers(1, 201, 400)]
+    mels = [(rng.standard_normal((f, 128)) - 3.0).astype(np.float32) for f in Fs]
+    fo = np.concatenate([[0], np.cumsum(Fs)])
+    g = ae.subsample(m, cuda(np.concatenate(mels)), fo).float().cpu().numpy()
+    off, worst = 0, 0.0
+    for mm, f in zip(mels, Fs):
+        want = oracle.subsample(mm, W)
+        t = want.shape[0]
+        r = rel_l2(g[off:off + t], want)
+        worst = max(worst, r)
+        assert r <= BF16_TOL, (f, r)
+        off += t
+    assert off == g.shape[0]
+    say(f"    worst clip rel {worst:.3e}")
+
+
 def test_layer_tone_fp32(model1_f32):
     say("[gpu] conformer_layer: 1 layer on the tone clip's tokens, fp32")
     W = weights(1)
