@@ -410,8 +410,25 @@ hipError_t mel_tables_init() {
 hipError_t launch_logmel(const float* wave, const int64_t* sample_off, const int64_t* frame_off,
                          int B, int64_t total_frames, float* mel, hipStream_t s) {
   if (total_frames <= 0) return hipSuccess;
+  // One round of blocks, three per CU (the block's 51.8 KB of LDS allows no
+  // more), each walking an equal run of frames, so every block sets up its
+  // registers and tables once: 32 x 30 s took 52.5 us against 59.4 for a
+  // grid of up to 4096 blocks (two groups each), 256 x 30 s 374 against
+  // 381 us; two and three rounds measured in between.
+  static int cus[64] = {0};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  if (cus[dev] == 0) {
+    int v = 0;
+    if ((e = hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess)
+      return e;
+    cus[dev] = v > 0 ? v : 1;
+  }
   const int64_t blocks = (total_frames + FPB - 1) / FPB;
-  const int grid = (int)(blocks < 4096 ? blocks : 4096);
+  const int64_t slots = 3 * (int64_t)cus[dev];
+  const int grid = (int)(blocks < slots ? blocks : slots);
   hipLaunchKernelGGL(k_logmel, dim3(grid), dim3(256), 0, s, wave, sample_off, frame_off, B,
                      total_frames, mel);
   return hipGetLastError();
