@@ -221,19 +221,20 @@ __device__ __forceinline__ f32x16 mfma16(uint4 a, uint4 b, f32x16 c) {
 // byte offset of 16-byte chunk c of staged row r
 __device__ __forceinline__ int srow(int r, int c) { return r * mf::RB + ((c ^ (r & 15)) << 4); }
 
-// The head is the grid's fast axis: blocks are dealt to the eight XCDs in
-// turn, so with eight heads every token block of one head runs on one XCD,
-// whose L2 then serves the K and V rows a block shares with the block
-// before it (47.5 against 49.3 us a layer with the token block on the fast
-// axis). tb0 is the first token block of the launch.
+// Block b takes head b % heads of token block b / heads. Blocks are dealt
+// to the eight XCDs in turn, so with eight heads every token block of one
+// head runs on one XCD, whose L2 then serves the K and V rows a block
+// shares with the block before it (47.5 against 49.3 us a layer with the
+// token block as the fast index).
 __global__ void __launch_bounds__(256, 2) k_attn_mfma(
     const bf16* __restrict__ qkv, const bf16* __restrict__ Rb, const int32_t* __restrict__ pos,
-    int64_t n, int d, int left, float cap, float lo, float hi, int64_t tb0, bf16* __restrict__ o) {
+    int64_t n, int d, int left, float cap, float lo, float hi, bf16* __restrict__ o) {
   using namespace mf;
   __shared__ __attribute__((aligned(1024))) unsigned char X[(KROWS + 16) * RB];
   __shared__ __attribute__((aligned(1024))) unsigned char Wr[NWAVE * WBYTES];
-  const int h = blockIdx.x;
-  const int64_t t0 = (tb0 + (int64_t)blockIdx.y) * QB;
+  const int heads = d / HD;
+  const int h = (int)(blockIdx.x % (unsigned)heads);
+  const int64_t t0 = (int64_t)(blockIdx.x / (unsigned)heads) * QB;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r32 = lane & 31, hf = lane >> 5;
@@ -410,17 +411,11 @@ hipError_t launch_attention(ae_dtype dt, const void* qkv, const void* R, const i
   if (n <= 0) return hipSuccess;
   if (d != heads * HD || left > MAXL || left < 1) return hipErrorInvalidValue;
   if (dt == AE_BF16) {
-    // token blocks in launches of at most 32768 (the grid's y extent is limited)
-    const int64_t nblk = (n + mf::QB - 1) / mf::QB;
-    for (int64_t b0 = 0; b0 < nblk; b0 += 32768) {
-      const int64_t nb = nblk - b0 < 32768 ? nblk - b0 : 32768;
-      hipLaunchKernelGGL(k_attn_mfma, dim3(heads, (unsigned)nb), dim3(256), 0, s,
-                         (const bf16*)qkv, (const bf16*)R, pos, n, d, left, softcap, lo, hi, b0,
-                         (bf16*)o);
-      const hipError_t e = hipGetLastError();
-      if (e != hipSuccess) return e;
-    }
-    return hipSuccess;
+    const int64_t blocks = (n + mf::QB - 1) / mf::QB * heads;
+    if (blocks > (int64_t)(UINT32_MAX / 256)) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_attn_mfma, dim3((unsigned)blocks), dim3(256), 0, s, (const bf16*)qkv,
+                       (const bf16*)R, pos, n, d, left, softcap, lo, hi, (bf16*)o);
+    return hipGetLastError();
   }
   hipLaunchKernelGGL(k_attn_f32, dim3((unsigned)((n + f32k::QB - 1) / f32k::QB), heads),
                      dim3(4 * f32k::QB), 0, s, (const float*)qkv, (const float*)R, pos, n, d, left,

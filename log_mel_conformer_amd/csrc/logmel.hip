@@ -33,6 +33,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <atomic>
 #include <mutex>
 #include <vector>
 
@@ -415,19 +416,21 @@ hipError_t launch_logmel(const float* wave, const int64_t* sample_off, const int
   // registers and tables once: 32 x 30 s took 52.5 us against 59.4 for a
   // grid of up to 4096 blocks (two groups each), 256 x 30 s 374 against
   // 381 us; two and three rounds measured in between.
-  static int cus[64] = {0};
+  static std::atomic<int> cus[64];  // per device, 0 until first asked
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-  if (cus[dev] == 0) {
+  int n_cu = cus[dev].load(std::memory_order_relaxed);
+  if (n_cu == 0) {
     int v = 0;
     if ((e = hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess)
       return e;
-    cus[dev] = v > 0 ? v : 1;
+    n_cu = v > 0 ? v : 1;
+    cus[dev].store(n_cu, std::memory_order_relaxed);
   }
   const int64_t blocks = (total_frames + FPB - 1) / FPB;
-  const int64_t slots = 3 * (int64_t)cus[dev];
+  const int64_t slots = 3 * (int64_t)n_cu;
   const int grid = (int)(blocks < slots ? blocks : slots);
   hipLaunchKernelGGL(k_logmel, dim3(grid), dim3(256), 0, s, wave, sample_off, frame_off, B,
                      total_frames, mel);

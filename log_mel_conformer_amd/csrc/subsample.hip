@@ -23,6 +23,8 @@
 //    them for 8 of the positions, normalises and stores them.
 // Rows outside the clip (before it or past its last conv0 row) and
 // frequencies outside 0 .. 63 are zero padding: masked where gathered.
+#include <atomic>
+
 #include "launch.h"
 
 namespace ae {
@@ -281,18 +283,20 @@ hipError_t launch_subsample_fused(const float* mel, const int64_t* frame_off,
   // One round of blocks, two per CU, each walking an equal run of tokens:
   // for 24000 tokens 48 a block took 217 us, against 226 for 16, 240 for 8
   // and 257 for 32 (1.5 rounds of the CUs)
-  static int cus[64] = {0};
+  static std::atomic<int> cus[64];  // per device, 0 until first asked
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-  if (cus[dev] == 0) {
+  int n_cu = cus[dev].load(std::memory_order_relaxed);
+  if (n_cu == 0) {
     int v = 0;
     if ((e = hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess)
       return e;
-    cus[dev] = v > 0 ? v : 1;
+    n_cu = v > 0 ? v : 1;
+    cus[dev].store(n_cu, std::memory_order_relaxed);
   }
-  const int64_t slots = 2 * (int64_t)cus[dev];
+  const int64_t slots = 2 * (int64_t)n_cu;
   const int run = (int)((n_tok + slots - 1) / slots);
   const unsigned grid = (unsigned)((n_tok + run - 1) / run);
   hipLaunchKernelGGL(k_subsample, dim3(grid), dim3(256), 0, s, mel, frame_off, row_off, tok_pos,
