@@ -301,18 +301,55 @@ def bench_merge(args, torch, ae, synth):
     print(json.dumps(rec), flush=True)
 
 
-def lfm2a_flops_per_launch(kclass, token_counts):
-    """Algorithmic flops of one launch of an LFM2A kernel class over the
-    batch: the feed-forward GEMMs are 2 T d n_ff; the attention per clip
-    and head takes q.k, (q + v).p on the t x t (query, key) pairs and
-    softmax.v, 2 t^2 head_dim each."""
+def lfm2a_work(sample_counts, frame_counts, token_counts, blocks=17):
+    """Algorithmic work per step of each LFM2A kernel class: (bound, amount)
+    with flops for the matrix-core and vector classes and bytes for the
+    memory-bound ones.
+    - front end: the samples read once (4 B); the 128-band feature plane
+      (512 B a frame) written; the frames the statistics cover (n // 160 of
+      a clip's 1 + n // 160) read for them and read again to normalise;
+      every frame written by the normalisation (the rest as zeros);
+    - stem convolutions (vector units): 9 multiply-adds per output value of
+      the 3x3 layer 0 (one input channel, 256 out) and of the two depthwise
+      layers; a 3x3 stride-2 layer with one row of padding maps h rows to
+      ceil(h / 2), and frequencies go 128 -> 64 -> 32 -> 16;
+    - GEMMs 2 M N K: the stem's two pointwise layers (256 -> 256 over
+      (rows, frequency)) and pre_encode_out (4096 -> 512); per block two
+      feed-forward pairs (512 -> 2048 -> 512), q|k|v (512 -> 1536), the
+      position projection of the 2 t_max - 1 table rows, the attention
+      output (512 -> 512), pw1 (512 -> 1024) and pw2 (512 -> 512); the
+      adapter (512 -> 2048 -> 2048);
+    - attention per clip of t tokens and block: q.k, (q + v).p and
+      softmax.v over the t x t pairs, 2 t^2 512 flops each;
+    - LayerNorms: one ahead of block 0 (x in, bf16 out: 6 B a value), three
+      of that kind per block and the block's closing norm, which writes x
+      back and the next norm's bf16 output (10 B);
+    - depthwise convolution: the GLU output in, its output out (bf16)."""
+    S, F = float(sum(sample_counts)), float(sum(frame_counts))
+    E = float(sum(int(n) // 160 for n in sample_counts))
     T = float(sum(token_counts))
-    d, ff = 512, 2048
-    if kclass in ("lfm_gemm_ffn1", "lfm_gemm_ffn2"):
-        return 2.0 * T * d * ff
-    if kclass == "lfm_attn":
-        return sum(6.0 * t * t * d for t in token_counts)
-    raise SystemExit(f"bench.py: no flop count for kernel class {kclass}")
+    up = lambda h: (h + 1) // 2  # noqa: E731
+    r1 = [up(f) for f in frame_counts]
+    r2 = [up(r) for r in r1]
+    R1, R2 = float(sum(r1)), float(sum(r2))
+    t_max = max(token_counts) if token_counts else 0
+    d, ff, ch, L = 512, 2048, 256, blocks
+    gemm = lambda m, n, k: 2.0 * m * n * k  # noqa: E731
+    return {
+        "lfm_front": ("hbm", 4.0 * S + 512.0 * (2 * F + 2 * E)),
+        "lfm_stem": ("alu", 2.0 * 9 * ch * (R1 * 64 + R2 * 32 + T * 16)),
+        "lfm_gemm_stem": ("mfma", gemm(R2 * 32, ch, ch) + gemm(T * 16, ch, ch)
+                          + gemm(T, d, 16 * ch)),
+        "lfm_gemm_ffn1": ("mfma", L * 2 * gemm(T, ff, d)),
+        "lfm_gemm_ffn2": ("mfma", L * 2 * gemm(T, d, ff)),
+        "lfm_gemm_attn": ("mfma", L * (gemm(T, 3 * d, d) + gemm(2 * t_max - 1, d, d)
+                                       + gemm(T, d, d))),
+        "lfm_gemm_conv": ("mfma", L * (gemm(T, 2 * d, d) + gemm(T, d, d))),
+        "lfm_gemm_adapter": ("mfma", gemm(T, 2048, d) + gemm(T, 2048, 2048)),
+        "lfm_attn": ("mfma", L * sum(6.0 * t * t * d for t in token_counts)),
+        "lfm_ln": ("hbm", T * d * (6.0 + L * (3 * 6.0 + 10.0))),
+        "lfm_dwconv": ("hbm", L * T * d * 2 * 2.0),
+    }
 
 
 def bench_lfm2a(args, torch, ae, synth):
@@ -351,10 +388,23 @@ def bench_lfm2a(args, torch, ae, synth):
     if args.copy_probe:
         copy_probe(torch)
     avg_ms = kms / max(launches, 1)
-    achieved = lfm2a_flops_per_launch(kclass, toks) / (avg_ms / 1e3) / 1e12
-    roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-            "frac": achieved / PEAK_BF16_TFLOPS, "traffic": recorded_traffic(kclass, args.workload),
-            "kernel": kclass, "avg_ms": avg_ms, "launches": launches}
+    work = lfm2a_work(np.diff(so), np.diff(pl["frame_off"]), toks)
+    bound, amount = work[kclass]
+    per_launch = amount / max(launches // args.steps, 1)
+    if bound == "hbm":
+        achieved = per_launch / (avg_ms / 1e3) / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    else:
+        peak = PEAK_F32_TFLOPS if bound == "alu" else PEAK_BF16_TFLOPS
+        achieved = per_launch / (avg_ms / 1e3) / 1e12
+        roof = {"bound": bound, "achieved": achieved, "peak": peak, "unit": "TFLOP/s"}
+    roof.update({"frac": achieved / roof["peak"],
+                 "traffic": recorded_traffic(kclass, args.workload), "kernel": kclass,
+                 "work_per_launch": per_launch, "avg_ms": avg_ms, "launches": launches})
+    table = None
+    if not args.no_kernel_table:
+        log("[bench] per-kernel events, one class at a time")
+        table = kernel_table(ae, torch, step, work, 3, PEAK_BF16_TFLOPS)
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline: the LFM2A oracle on one clip")
@@ -377,7 +427,7 @@ def bench_lfm2a(args, torch, ae, synth):
                       "global_batch": len(clips), "seq_len": max(toks), "tokens": tokens,
                       "frames": frames, "audio_seconds": audio_s,
                       "tokens_per_s": tokens / (ms / 1e3), "parallelism": "none (1 GPU)"},
-           "roofline": roof, "cpu_baseline": cpu}
+           "roofline": roof, "kernels": table, "cpu_baseline": cpu}
     add_copy_denominator(rec["roofline"], torch)
     print(json.dumps(rec), flush=True)
 
@@ -443,7 +493,9 @@ def encoder_work(pl, cfg, es, layers, q8=False, head=True):
 
 def kernel_table(ae, torch, step, work, steps, peak_mm):
     """One pass per kernel class with HIP events around its launches alone:
-    average launch time, achieved rate and fraction of the roofline."""
+    average launch time, achieved rate and fraction of the roofline (the
+    matrix cores' peak for "mfma", the fp32 vector peak for "alu", HBM for
+    "hbm")."""
     out = []
     for cls, (bound, amount) in work.items():
         ae.timing_enable(cls)
@@ -455,9 +507,9 @@ def kernel_table(ae, torch, step, work, steps, peak_mm):
         if launches == 0:
             continue
         per_step_ms = kms / steps
-        if bound == "mfma":
+        if bound in ("mfma", "alu"):
             ach = amount / (per_step_ms / 1e3) / 1e12
-            peak, unit = peak_mm, "TFLOP/s"
+            peak, unit = (peak_mm if bound == "mfma" else PEAK_F32_TFLOPS), "TFLOP/s"
         else:
             ach = amount / (per_step_ms / 1e3) / 1e9
             peak, unit = PEAK_HBM_GBS, "GB/s"

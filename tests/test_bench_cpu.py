@@ -106,3 +106,48 @@ def test_encoder_work_matches_independent_counts():
     assert abs(w["rownorm"][1] - T * sum(launches)) < 1.0
     assert w["logmel"][1] == 4.0 * S + 512.0 * F
     assert w["attn"][1] == 12 * T * 4 * es * d and w["lconv"][1] == 12 * T * 2 * es * d
+
+
+def test_lfm2a_work_matches_independent_counts():
+    """The LFM2A work model against a launch-by-launch count built from the
+    oracle's geometry (frames, conv_out, tokens): 32 clips of 30 s."""
+    from oracle import lfm2a as olfm
+    n = [480000] * 31 + [123457]
+    F = [olfm.num_frames(x) for x in n]
+    T = [olfm.num_tokens(x) for x in n]
+    w = bench.lfm2a_work(n, F, T)
+    d, ff, L = 512, 2048, 17
+    r1 = [olfm.conv_out(f, 3, 2, 1) for f in F]
+    r2 = [olfm.conv_out(r, 3, 2, 1) for r in r1]
+    assert [olfm.conv_out(r, 3, 2, 1) for r in r2] == T
+    Tn, R1, R2 = sum(T), sum(r1), sum(r2)
+    assert T[0] == 376 and Tn == 31 * 376 + T[-1]
+    mm = lambda m, nn, k: 2.0 * m * nn * k  # noqa: E731
+    # stem: three 3x3 layers, 9 multiply-adds per output value, 256 channels
+    assert w["lfm_stem"] == ("alu", 2 * 9 * 256 * (R1 * 64 + R2 * 32 + Tn * 16.0))
+    assert w["lfm_gemm_stem"][1] == mm(R2 * 32, 256, 256) + mm(Tn * 16, 256, 256) + mm(Tn, 512, 4096)
+    # per block: ffn, attention (q|k|v, position rows, output), conv (pw1, pw2), ffn
+    launches = {"lfm_gemm_ffn1": 0.0, "lfm_gemm_ffn2": 0.0, "lfm_gemm_attn": 0.0,
+                "lfm_gemm_conv": 0.0}
+    for _ in range(L):
+        for _half in range(2):
+            launches["lfm_gemm_ffn1"] += mm(Tn, ff, d)
+            launches["lfm_gemm_ffn2"] += mm(Tn, d, ff)
+        launches["lfm_gemm_attn"] += mm(Tn, 3 * d, d) + mm(2 * max(T) - 1, d, d) + mm(Tn, d, d)
+        launches["lfm_gemm_conv"] += mm(Tn, 2 * d, d) + mm(Tn, d, d)
+    for k, v in launches.items():
+        assert abs(w[k][1] - v) <= 1e-9 * v, k
+    assert w["lfm_gemm_adapter"][1] == mm(Tn, 2048, 512) + mm(Tn, 2048, 2048)
+    assert w["lfm_attn"][1] == L * sum(3 * 2.0 * t * t * d for t in T)
+    # 69 LayerNorm launches: one before block 0, four per block; the last of
+    # each block writes x back besides the next norm's bf16 output
+    ln = [(4 + 2) * d]
+    for _ in range(L):
+        ln += [(4 + 2) * d] * 3 + [(4 + 4 + 2) * d]
+    assert len(ln) == 69 and w["lfm_ln"] == ("hbm", Tn * float(sum(ln)))
+    assert w["lfm_dwconv"] == ("hbm", L * Tn * (2 + 2) * d * 1.0)
+    # front end: samples in; every frame written twice (features, then the
+    # normalised or zeroed plane); the statistics frames read twice
+    E = [olfm.effective_frames(x) for x in n]
+    assert all(e == f - 1 for e, f in zip(E, F))
+    assert w["lfm_front"] == ("hbm", 4.0 * sum(n) + 512.0 * (2 * sum(F) + 2 * sum(E)))
