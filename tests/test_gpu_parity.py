@@ -253,6 +253,29 @@ def test_layer_packed_positions_bf16():
         off += n
 
 
+def test_layer_attention_block_edges_bf16():
+    """The bf16 attention takes 128 tokens a block: clips of 127, 128 and
+    129 tokens, then clips of 12 and 13 (one just fills the window, one
+    just exceeds it), one of 256 and a single token, packed so that clip
+    starts fall at varied offsets inside the blocks and a block's staged
+    keys reach back into the previous clip; each clip against the oracle."""
+    say("[gpu] conformer_layer: clips of 127/128/129/12/13/256/1 tokens at block edges, bf16")
+    W = weights(1, bf16=True)
+    m = ae.Model(W, dtype="bf16")
+    rng = np.random.default_rng(128)
+    lens = [127, 128, 129, 12, 13, 256, 1]
+    h0 = rng.standard_normal((sum(lens), 1024)).astype(np.float32)
+    pos = np.concatenate([np.arange(n) for n in lens]).astype(np.int32)
+    h = cuda(h0)
+    ae.conformer_layer(m, 0, h, cuda(pos, torch.int32))
+    g = h.cpu().numpy()
+    off = 0
+    for n in lens:
+        want = oracle.conformer_layer(h0[off:off + n], W["layers"][0], np.arange(n, dtype=np.int32))
+        bf16_gate(g[off:off + n], want, f"{n} tokens at {off}")
+        off += n
+
+
 @pytest.mark.parametrize("total", [16383, 16384, 16385])
 def test_layer_row_count_across_tile_rules_bf16(total):
     """The bf16 projections pick their tiles by row count: below 16384 rows
