@@ -452,6 +452,24 @@ def test_clip_isolation_and_determinism_bf16():
         off += t
 
 
+def test_overlong_clip_truncated_bf16():
+    """A clip past 30 s is encoded as its first 480000 samples: the 31 s
+    clip, alone and packed between two short clips, gives the bits of its
+    30 s prefix."""
+    say("[gpu] invariant: a 31 s clip encodes as its first 30 s, bf16")
+    W = weights(12, bf16=True)
+    m = ae.Model(W, dtype="bf16")
+    x = synth.multisine_clip(31, 496000)
+    a = ae.encode(m, cuda(x), np.array([0, len(x)])).cpu().numpy()
+    b = ae.encode(m, cuda(x[:480000].copy()), np.array([0, 480000])).cpu().numpy()
+    assert a.shape == (750, 512) and np.array_equal(a, b)
+    clips = [synth.tone_clip(5, 20000), x, synth.tone_clip(6, 9000)]
+    wave, so = synth.pack(clips)
+    packed = ae.encode(m, cuda(wave), so).cpu().numpy()
+    t0 = ae.num_tokens(20000)
+    assert np.array_equal(packed[t0:t0 + 750], b)
+
+
 def test_empty_batches():
     say("[gpu] edge: empty batch, clips without tokens")
     W = weights(1)
