@@ -452,6 +452,25 @@ def test_clip_isolation_and_determinism_bf16():
         off += t
 
 
+def test_clip_isolation_fp32():
+    """The fp32 path keeps a clip's output bit-identical alone and packed
+    too (its attention sums the window in a fixed order, its GEMMs
+    accumulate every output in the same k order whatever its row)."""
+    say("[gpu] invariant: clip isolation in a pack, fp32, 2 layers + head")
+    W = weights(2)
+    m = ae.Model(W, dtype="f32")
+    clips = [synth.pink_clip(3, 30000), synth.multisine_clip(7, 50000), synth.tone_clip(8, 12000)]
+    wave, so = synth.pack(clips)
+    packed = ae.encode(m, cuda(wave), so).cpu().numpy()
+    off = 0
+    for c in clips:
+        t = ae.num_tokens(len(c))
+        alone = ae.encode(m, cuda(c), np.array([0, len(c)])).cpu().numpy()
+        assert np.array_equal(alone, packed[off:off + t])
+        off += t
+    assert off == packed.shape[0]
+
+
 def test_overlong_clip_truncated_bf16():
     """A clip past 30 s is encoded as its first 480000 samples: the 31 s
     clip, alone and packed between two short clips, gives the bits of its
