@@ -455,7 +455,8 @@ def test_clip_isolation_and_determinism_bf16():
 def test_clip_isolation_fp32():
     """The fp32 path keeps a clip's output bit-identical alone and packed
     too (its attention sums the window in a fixed order, its GEMMs
-    accumulate every output in the same k order whatever its row)."""
+    accumulate every output in the same k order whatever its row and
+    whichever tile shape the row count selects)."""
     say("[gpu] invariant: clip isolation in a pack, fp32, 2 layers + head")
     W = weights(2)
     m = ae.Model(W, dtype="f32")
@@ -469,6 +470,14 @@ def test_clip_isolation_fp32():
         assert np.array_equal(alone, packed[off:off + t])
         off += t
     assert off == packed.shape[0]
+    # a pack past 4096 rows runs its GEMMs in the large-row tiles: the same
+    # bits again for the clip that also ran alone
+    big = [synth.multisine_clip(20 + i) for i in range(6)] + [clips[1]]
+    wave, so = synth.pack(big)
+    packed = ae.encode(m, cuda(wave), so).cpu().numpy()
+    assert packed.shape[0] == 6 * 750 + ae.num_tokens(len(clips[1]))
+    alone = ae.encode(m, cuda(clips[1]), np.array([0, len(clips[1])])).cpu().numpy()
+    assert np.array_equal(alone, packed[6 * 750:])
 
 
 def test_overlong_clip_truncated_bf16():
