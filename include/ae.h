@@ -226,7 +226,7 @@ ae_status ae_encode(const ae_model* m, const float* wave, const int64_t* sample_
  * looks up the array's device address once).
  * Errors: AE_ERR_CAPACITY when the batch needs more than
  * AE_STATIC_SCRATCH_BYTES (what ae_workspace_bytes reports for it; one 30 s
- * clip needs about 35 MB in bf16, 110 MB in f32); AE_ERR_INVALID for a
+ * clip needs about 35 MB in bf16, 122 MB in f32); AE_ERR_INVALID for a
  * device mismatch or NULL pointers; as ae_encode otherwise.
  * Calls on one device share the array and the last call's contents stay
  * in it; every buffer in it is written before it is read within a call, so

@@ -352,6 +352,8 @@ struct Ws {
   float* o1 = nullptr;
   void* on = nullptr;
   void* dq = nullptr;  // int8 models: one layer's projections widened to bf16
+  float* part = nullptr;  // float models: partial tiles of FFN W2's K split
+  size_t part_bytes = 0;
   size_t total = 0;
 };
 
@@ -386,6 +388,11 @@ Ws ws_layout(const ae_model* m, int B, int64_t F, int64_t T, char* base) {
   w.o1 = (float*)take(sizeof(float) * (size_t)T * m->cfg.out_hidden);
   w.on = take(es * (size_t)T * m->cfg.out_hidden);
   if (m->q8) w.dq = take(2 * (4 * (size_t)m->cfg.ff * d + 7 * d * d));
+  if (m->dt != AE_BF16) {
+    // FFN W2 (K = ff) is the one float projection deep enough to split
+    w.part_bytes = gemm_f32_part_bytes(T, (int)d, m->cfg.ff);
+    if (w.part_bytes) w.part = (float*)take(w.part_bytes);
+  }
   w.total = off;
   return w;
 }
@@ -402,10 +409,13 @@ Ws ws_layout(const ae_model* m, int B, int64_t F, int64_t T, char* base) {
 
 const float kInf = INFINITY;
 
-GemmParams gemm_params(int M, int N, int K, const void* A, int lda, const void* B, int ldb,
-                       void* C, int ldc) {
+// w: the call's workspace, whose K-split area (float models) the GEMM may use
+GemmParams gemm_params(const Ws& w, int M, int N, int K, const void* A, int lda, const void* B,
+                       int ldb, void* C, int ldc) {
   GemmParams p;
   memset(&p, 0, sizeof(p));
+  p.part = w.part;
+  p.part_bytes = w.part_bytes;
   p.M = M; p.N = N; p.K = K;
   p.A[0] = p.A[1] = p.A[2] = A;
   p.lda = lda;
@@ -460,8 +470,8 @@ ae_status subsample_impl(const ae_model* m, const float* mel, const Plan& pl, co
   } else {
     AE_LAUNCH(AE_K_CONV0, s, launch_conv0(m->dt, mel, d_frame, d_row, B, pl.rows(), m->w.conv0,
                                           m->w.ln0, w.y0, s));
-    GemmParams p = gemm_params((int)(T * 32), kC1, kC0 * 9, nullptr, 0, m->conv1r, kC0 * 9, w.x1,
-                               kC1);
+    GemmParams p = gemm_params(w, (int)(T * 32), kC1, kC0 * 9, nullptr, 0, m->conv1r, kC0 * 9,
+                               w.x1, kC1);
     p.y0 = w.y0;
     p.row_off = d_row;
     p.tok_pos = w.tok_pos;
@@ -471,7 +481,8 @@ ae_status subsample_impl(const ae_model* m, const float* mel, const Plan& pl, co
     AE_LAUNCH(AE_K_CONV1, s, launch_gemm(m->dt, EPI_LNRELU, A_CONV1, true, p, s));
   }
   const int d = m->cfg.hidden;
-  GemmParams q = gemm_params((int)T, d, kC1 * kF2, w.x1, kC1 * kF2, m->w.in_proj, kC1 * kF2, x, d);
+  GemmParams q =
+      gemm_params(w, (int)T, d, kC1 * kF2, w.x1, kC1 * kF2, m->w.in_proj, kC1 * kF2, x, d);
   AE_LAUNCH(AE_K_GEMM_HEAD, s, launch_gemm(m->dt, EPI_STORE, A_PLAIN, false, q, s));
   return AE_OK;
 }
@@ -525,11 +536,11 @@ ae_status layer_impl(const ae_model* m, int l, float* h, const int32_t* pos, int
       r.w_next = pre; r.n_out = 1; r.a[0] = w.a[0]; r.lo[0] = c1.in_lo; r.hi[0] = c1.in_hi;
       AE_LAUNCH(AE_K_ROWNORM, s, launch_rownorm(dt, r, s));
     }
-    GemmParams p1 = gemm_params(M, ff, d, w.a[0], d, w1, d, w.u, ff);
+    GemmParams p1 = gemm_params(w, M, ff, d, w.a[0], d, w1, d, w.u, ff);
     set_out_clip(p1, c1);
     p1.nlo = c2.in_lo; p1.nhi = c2.in_hi;
     AE_LAUNCH(AE_K_GEMM_FFN1, s, launch_gemm(dt, EPI_SILU, A_PLAIN, lowp, p1, s));
-    GemmParams p2 = gemm_params(M, d, ff, w.u, ff, w2, ff, w.y, d);
+    GemmParams p2 = gemm_params(w, M, d, ff, w.u, ff, w2, ff, w.y, d);
     set_out_clip(p2, c2);
     AE_LAUNCH(AE_K_GEMM_FFN2, s, launch_gemm(dt, EPI_STORE, A_PLAIN, lowp, p2, s));
     return AE_OK;
@@ -555,7 +566,7 @@ ae_status layer_impl(const ae_model* m, int l, float* h, const int32_t* pos, int
   }
   // ---- attention: fused q|k|v projection with per-column q/k scaling
   {
-    GemmParams p = gemm_params(M, 3 * d, d, w.a[0], d, L.q, d, w.qkv, 3 * d);
+    GemmParams p = gemm_params(w, M, 3 * d, d, w.a[0], d, L.q, d, w.qkv, 3 * d);
     const int nout = m->attn_nout[l];
     p.A[1] = nout == 1 ? w.a[0] : w.a[1];
     p.A[2] = nout == 1 ? w.a[0] : w.a[2];
@@ -572,7 +583,7 @@ ae_status layer_impl(const ae_model* m, int l, float* h, const int32_t* pos, int
                              m->cfg.heads, m->left, m->cfg.softcap, L.post_clip.in_lo,
                              L.post_clip.in_hi, w.o, s));
   {
-    GemmParams p = gemm_params(M, d, d, w.o, d, L.post, d, w.y, d);
+    GemmParams p = gemm_params(w, M, d, d, w.o, d, L.post, d, w.y, d);
     set_out_clip(p, L.post_clip);
     AE_LAUNCH(AE_K_GEMM_POST, s, launch_gemm(dt, EPI_STORE, A_PLAIN, lowp, p, s));
   }
@@ -585,7 +596,7 @@ ae_status layer_impl(const ae_model* m, int l, float* h, const int32_t* pos, int
   }
   // ---- light conv
   {
-    GemmParams p = gemm_params(M, 2 * d, d, w.a[0], d, L.lc_start, d, w.g, d);
+    GemmParams p = gemm_params(w, M, 2 * d, d, w.a[0], d, L.lc_start, d, w.g, d);
     set_out_clip(p, L.lc_start_clip);
     p.glu_d = d;
     AE_LAUNCH(AE_K_GEMM_LCSTART, s, launch_gemm(dt, EPI_GLU, A_PLAIN, lowp, p, s));
@@ -598,7 +609,7 @@ ae_status layer_impl(const ae_model* m, int l, float* h, const int32_t* pos, int
   // it to h (the light conv's residual has no norm) while the row is in
   // registers, so the GEMM's epilogue does not wait on reading h
   {
-    GemmParams p = gemm_params(M, d, d, w.c, d, L.lc_end, d, w.y, d);
+    GemmParams p = gemm_params(w, M, d, d, w.c, d, L.lc_end, d, w.y, d);
     set_out_clip(p, L.lc_end_clip);
     AE_LAUNCH(AE_K_GEMM_LCEND, s, launch_gemm(dt, EPI_STORE, A_PLAIN, lowp, p, s));
   }
@@ -1069,7 +1080,7 @@ ae_status encode_impl(const ae_model* m, const float* wave, const Plan& pl, floa
   const int oh = m->cfg.out_hidden, od = m->cfg.out_dim;
   {
     const void* hin = m->dt == AE_BF16 ? w.a[0] : (const void*)w.h;
-    GemmParams p = gemm_params((int)T, oh, d, hin, d, m->w.out_proj, d, w.o1, oh);
+    GemmParams p = gemm_params(w, (int)T, oh, d, hin, d, m->w.out_proj, d, w.o1, oh);
     p.bias = m->w.out_bias;
     AE_LAUNCH(AE_K_GEMM_HEAD, s, launch_gemm(m->dt, EPI_BIAS, A_PLAIN, false, p, s));
   }
@@ -1082,7 +1093,7 @@ ae_status encode_impl(const ae_model* m, const float* wave, const Plan& pl, floa
     AE_LAUNCH(AE_K_ROWNORM, s, launch_rownorm(m->dt, r, s));
   }
   {
-    GemmParams p = gemm_params((int)T, od, oh, w.on, oh, m->w.embed, oh, out, od);
+    GemmParams p = gemm_params(w, (int)T, od, oh, w.on, oh, m->w.embed, oh, out, od);
     AE_LAUNCH(AE_K_GEMM_HEAD, s, launch_gemm(m->dt, EPI_STORE, A_PLAIN, false, p, s));
   }
   return AE_OK;

@@ -402,7 +402,12 @@ __global__ void __launch_bounds__(WM * WN * 64) k_gemm(GemmParams p) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
   const int tiles_n = p.N / BN;
-  const int tm = blockIdx.x / tiles_n, tn = blockIdx.x - tm * tiles_n;
+  // a K split: block b takes tile b % tiles and the split-th share of the
+  // k-steps, and leaves its partial tile for k_gemm_reduce
+  const int splits = p.splits > 1 ? p.splits : 1;
+  const int tiles = ((p.M + BM - 1) / BM) * tiles_n;
+  const int tile = (int)blockIdx.x % tiles, split = (int)blockIdx.x / tiles;
+  const int tm = tile / tiles_n, tn = tile - tm * tiles_n;
   const int m0 = tm * BM, n0 = tn * BN;
 
   int seg = 0, nloc = n0;
@@ -501,13 +506,13 @@ __global__ void __launch_bounds__(WM * WN * 64) k_gemm(GemmParams p) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-  const int nk = p.K / BK;
-  load_global(0);
+  const int nk = p.K / BK / splits, k0 = split * nk;
+  load_global(k0);
   store_lds(0);
   __syncthreads();
   for (int kt = 0; kt < nk; ++kt) {
     const int cur = kt & 1;
-    if (kt + 1 < nk) load_global(kt + 1);
+    if (kt + 1 < nk) load_global(k0 + kt + 1);
     const unsigned char* s = smem + cur * STAGE;
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
@@ -528,6 +533,63 @@ __global__ void __launch_bounds__(WM * WN * 64) k_gemm(GemmParams p) {
     __syncthreads();
   }
 
+  if (splits > 1) {
+    float4* dst = (float4*)p.part +
+                  ((size_t)(split * tiles + tile) * (WM * WN) + wave) * (MT * NTL * 4 * 64) + lane;
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+      for (int j = 0; j < NTL; ++j)
+#pragma unroll
+        for (int v4 = 0; v4 < 4; ++v4)
+          dst[((i * NTL + j) * 4 + v4) * 64] =
+              make_float4(acc[i][j][4 * v4], acc[i][j][4 * v4 + 1], acc[i][j][4 * v4 + 2],
+                          acc[i][j][4 * v4 + 3]);
+    return;
+  }
+  epilogue<TO, MT, NTL, EPI>(p, acc, m0 + wm * WTM, n0 + wn * WTN, seg, lane);
+}
+
+// The second pass of a K split: each wavefront adds its accumulators' shares
+// from the p.splits partial tiles in split order (a fixed order, so the
+// result does not depend on which split finished first) and runs the
+// epilogue the one-pass kernel would have.
+template <typename TO, int BM, int BN, int WM, int WN, int EPI>
+__global__ void __launch_bounds__(WM * WN * 64) k_gemm_reduce(GemmParams p) {
+  constexpr int WTM = BM / WM, WTN = BN / WN;
+  constexpr int MT = WTM / 32, NTL = WTN / 32;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+  const int tiles_n = p.N / BN;
+  const int tiles = ((p.M + BM - 1) / BM) * tiles_n;
+  const int tile = blockIdx.x;
+  const int tm = tile / tiles_n, tn = tile - tm * tiles_n;
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int seg = (EPI != EPI_GLU && EPI != EPI_LNRELU) ? n0 / p.seg_n : 0;
+  f32x16 acc[MT][NTL];
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int j = 0; j < NTL; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+  for (int sp = 0; sp < p.splits; ++sp) {
+    const float4* src = (const float4*)p.part +
+                        ((size_t)(sp * tiles + tile) * (WM * WN) + wave) * (MT * NTL * 4 * 64) +
+                        lane;
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+      for (int j = 0; j < NTL; ++j)
+#pragma unroll
+        for (int v4 = 0; v4 < 4; ++v4) {
+          const float4 v = src[((i * NTL + j) * 4 + v4) * 64];
+          acc[i][j][4 * v4] += v.x;
+          acc[i][j][4 * v4 + 1] += v.y;
+          acc[i][j][4 * v4 + 2] += v.z;
+          acc[i][j][4 * v4 + 3] += v.w;
+        }
+  }
   epilogue<TO, MT, NTL, EPI>(p, acc, m0 + wm * WTM, n0 + wn * WTN, seg, lane);
 }
 
@@ -866,31 +928,67 @@ hipError_t run(const GemmParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
+// The float path's K split. A split count that followed the row count
+// would change each output's summation order between a clip run alone and
+// the same clip packed with others, so it follows K alone: the 4096-deep
+// FFN W2 (in a 30 s clip 192 64x64 tiles with 4096-deep k-loops, 768
+// wavefronts for 1024 SIMDs) runs as four splits of 1024, every other
+// projection (K of 1024 to 1536) whole. Each split leaves its partial tile
+// in p.part, and k_gemm_reduce adds them in split order and runs the
+// epilogue. The caller's area must hold splits x (M rounded up to the row
+// tile) x N floats; a smaller one is an error, not a silent unsplit run.
+// Measured on a 30 s clip: FFN W2 102.6 us whole, 83.7 in two splits, 66.7
+// in four (step 6.74 -> 6.21 -> 5.78 ms); on a 1 s clip 100.8, 55.0 and
+// 32.9 us. For large batches four splits add 32 bytes of partial traffic a
+// row and column pair (about 7% on a 24000-row W2).
+constexpr int kSplitK4096 = 4;
+int f32_splits(int K) { return K >= 4096 && K % 4096 == 0 ? kSplitK4096 * (K / 4096) : 1; }
+
+template <int BM, int BN, int WM, int WN, int EPI>
+hipError_t run_f32(const GemmParams& p0, hipStream_t s) {
+  if (p0.M <= 0) return hipSuccess;
+  GemmParams p = p0;
+  const int S = f32_splits(p.K);
+  p.splits = S;
+  if (S == 1) return run<float, float, BM, BN, WM, WN, A_PLAIN, EPI>(p, s);
+  const int tiles = ((p.M + BM - 1) / BM) * (p.N / BN);
+  if (!p.part || (size_t)S * tiles * BM * BN * sizeof(float) > p.part_bytes)
+    return hipErrorInvalidValue;
+  hipLaunchKernelGGL((k_gemm<float, float, BM, BN, WM, WN, A_PLAIN, EPI>), dim3(tiles * S),
+                     dim3(WM * WN * 64), 0, s, p);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((k_gemm_reduce<float, BM, BN, WM, WN, EPI>), dim3(tiles), dim3(WM * WN * 64),
+                     0, s, p);
+  return hipGetLastError();
+}
+
 // fp32 operands (the parity path): register-staged 128x128 tiles, or for
 // fewer than 4096 rows (a 30 s clip has 750 tokens, where 128x128 tiles
 // give a 1024-column output 48 blocks for 256 CUs) 64x64 tiles of four
 // 32x32 wavefronts (64x128 for the GLU, whose column pairs need 64-column
-// wavefront tiles).
+// wavefront tiles). Every tile shape accumulates an output over k in the
+// same order, so the shape, which follows the row count, changes no bit.
 hipError_t dispatch_f32(int epi, int aload, const GemmParams& p, hipStream_t s) {
   if (aload == A_CONV1) return run<float, float, 128, 32, 4, 1, A_CONV1, EPI_LNRELU>(p, s);
   if (p.M < 4096) {
     switch (epi) {
-      case EPI_STORE: return run<float, float, 64, 64, 2, 2, A_PLAIN, EPI_STORE>(p, s);
-      case EPI_SILU: return run<float, float, 64, 64, 2, 2, A_PLAIN, EPI_SILU>(p, s);
-      case EPI_GLU: return run<float, float, 64, 128, 2, 2, A_PLAIN, EPI_GLU>(p, s);
-      case EPI_RESID: return run<float, float, 64, 64, 2, 2, A_PLAIN, EPI_RESID>(p, s);
-      case EPI_BIAS: return run<float, float, 64, 64, 2, 2, A_PLAIN, EPI_BIAS>(p, s);
-      case EPI_ACT: return run<float, float, 64, 64, 2, 2, A_PLAIN, EPI_ACT>(p, s);
+      case EPI_STORE: return run_f32<64, 64, 2, 2, EPI_STORE>(p, s);
+      case EPI_SILU: return run_f32<64, 64, 2, 2, EPI_SILU>(p, s);
+      case EPI_GLU: return run_f32<64, 128, 2, 2, EPI_GLU>(p, s);
+      case EPI_RESID: return run_f32<64, 64, 2, 2, EPI_RESID>(p, s);
+      case EPI_BIAS: return run_f32<64, 64, 2, 2, EPI_BIAS>(p, s);
+      case EPI_ACT: return run_f32<64, 64, 2, 2, EPI_ACT>(p, s);
     }
     return hipErrorInvalidValue;
   }
   switch (epi) {
-    case EPI_STORE: return run<float, float, 128, 128, 2, 2, A_PLAIN, EPI_STORE>(p, s);
-    case EPI_SILU: return run<float, float, 128, 128, 2, 2, A_PLAIN, EPI_SILU>(p, s);
-    case EPI_GLU: return run<float, float, 128, 128, 2, 2, A_PLAIN, EPI_GLU>(p, s);
-    case EPI_RESID: return run<float, float, 128, 128, 2, 2, A_PLAIN, EPI_RESID>(p, s);
-    case EPI_BIAS: return run<float, float, 128, 128, 2, 2, A_PLAIN, EPI_BIAS>(p, s);
-    case EPI_ACT: return run<float, float, 128, 128, 2, 2, A_PLAIN, EPI_ACT>(p, s);
+    case EPI_STORE: return run_f32<128, 128, 2, 2, EPI_STORE>(p, s);
+    case EPI_SILU: return run_f32<128, 128, 2, 2, EPI_SILU>(p, s);
+    case EPI_GLU: return run_f32<128, 128, 2, 2, EPI_GLU>(p, s);
+    case EPI_RESID: return run_f32<128, 128, 2, 2, EPI_RESID>(p, s);
+    case EPI_BIAS: return run_f32<128, 128, 2, 2, EPI_BIAS>(p, s);
+    case EPI_ACT: return run_f32<128, 128, 2, 2, EPI_ACT>(p, s);
   }
   return hipErrorInvalidValue;
 }
@@ -958,6 +1056,12 @@ hipError_t dispatch_bf16(int epi, int aload, bool out_bf16, const GemmParams& p,
 }
 
 }  // namespace
+
+size_t gemm_f32_part_bytes(int64_t M, int N, int K) {
+  const int S = f32_splits(K);
+  if (S == 1 || M <= 0) return 0;
+  return (size_t)S * (size_t)((M + 127) / 128 * 128) * (size_t)N * sizeof(float);
+}
 
 hipError_t launch_gemm(ae_dtype dt, int epi, int aload, bool out_bf16, const GemmParams& p,
                        hipStream_t s) {

@@ -48,11 +48,19 @@ struct GemmParams {
   const float* gain;
   int act;                  // EPI_ACT: an ActKind
   float rscale;             // EPI_RESID: C += rscale * (acc + bias)
+  // float operands: a workspace area for the partial tiles of a K split,
+  // at least gemm_f32_part_bytes(M, N, K) bytes; splits is the dispatcher's
+  float* part;
+  size_t part_bytes;
+  int splits;
 };
 
 // dtype: AE_F32 or AE_BF16 operands; out_bf16: TO = bf16 (else float).
 hipError_t launch_gemm(ae_dtype dt, int epi, int aload, bool out_bf16, const GemmParams& p,
                        hipStream_t s);
+// Bytes of the K-split area a float GEMM of this shape needs (0: it runs
+// in one pass). The split count follows K alone.
+size_t gemm_f32_part_bytes(int64_t M, int N, int K);
 
 // -------------------------------------------------------------- front end
 hipError_t mel_tables_init();
