@@ -5,6 +5,7 @@
 #include <math.h>
 #include <string.h>
 
+#include <algorithm>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -389,8 +390,13 @@ Ws ws_layout(const ae_model* m, int B, int64_t F, int64_t T, char* base) {
   w.on = take(es * (size_t)T * m->cfg.out_hidden);
   if (m->q8) w.dq = take(2 * (4 * (size_t)m->cfg.ff * d + 7 * d * d));
   if (m->dt != AE_BF16) {
-    // FFN W2 (K = ff) is the one float projection deep enough to split
-    w.part_bytes = gemm_f32_part_bytes(T, (int)d, m->cfg.ff);
+    // the K-split area of the float projections: the largest any of them
+    // needs (with the tower's sizes only FFN W2, K = ff, splits)
+    const int di = (int)d, ff = m->cfg.ff, oh = m->cfg.out_hidden, od = m->cfg.out_dim;
+    const int shapes[8][2] = {{ff, di}, {di, ff}, {3 * di, di}, {2 * di, di},
+                              {di, di}, {di, kC1 * kF2}, {oh, di}, {od, oh}};  // {N, K}
+    for (const auto& nk : shapes)
+      w.part_bytes = std::max(w.part_bytes, gemm_f32_part_bytes(T, nk[0], nk[1]));
     if (w.part_bytes) w.part = (float*)take(w.part_bytes);
   }
   w.total = off;
