@@ -448,23 +448,30 @@ def encoder_work(pl, cfg, es, layers, q8=False, head=True):
     """Algorithmic work per step of each kernel class of ae_encode: (bound,
     amount) with flops for the matrix-core classes and bytes for the
     memory-bound ones. es = bytes per stored activation (2 bf16, 4 fp32).
-    Row kernels per layer: four launches that read a GEMM output y and h
-    and write h and the next normed input (after FFN 1, after attention,
+    Row kernels per layer: four launches (after FFN 1, after attention,
     the light conv's residual add with FFN 2's pre-norm, after FFN 2 with
-    norm_out); the first layer's FFN 1 pre-norm reads h and writes its
-    input; the last launch writes the head's bf16 copy of h instead of a
-    next input (nothing in fp32); the head's norm reads and writes 1536
-    columns."""
+    norm_out). In fp32 each reads a GEMM output y and h and writes h and
+    the next normed input. In bf16 they run in pairs: the first reads h and
+    its y and writes only the next input; the second reads h, the first's
+    y and its own, and writes h and the next input. The first layer's
+    FFN 1 pre-norm reads h and writes its input; the last launch writes the
+    head's bf16 copy of h instead of a next input (nothing in fp32); the
+    head's norm reads and writes 1536 columns."""
     T = float(pl["token_off"][-1])
     F = float(pl["frame_off"][-1])
     T1 = float(pl["row_off"][-1])
     S = float(pl["sample_off"][-1])
     d, ff, oh, od = cfg.hidden, cfg.ff, cfg.out_hidden, cfg.out_dim
     L = layers
-    post = (es + 8 + es) * d           # y in, h read and written, next input out
     pre = (4 + es) * d                  # h in, normed input out
-    last = (es + 8 + (es if es == 2 and head else 0)) * d
-    rows = pre + L * 4 * post - post + last + ((4 + es) * oh if head else 0)
+    if es == 2:
+        first = (4 + 2 * es) * d        # h and y in, next input out
+        second = (8 + 3 * es) * d       # h, y0 and y in; h and next input (or head copy) out
+        rows = pre + L * 2 * (first + second) - (0 if head else es * d)
+    else:
+        post = (es + 8 + es) * d        # y in, h read and written, next input out
+        rows = pre + L * 4 * post - es * d   # the last launch writes no next input
+    rows += (4 + es) * oh if head else 0
     w = {
         "logmel": ("hbm", 4.0 * S + 4.0 * 128 * F),
         "conv0": ("hbm", 4.0 * 128 * F + es * T1 * 64 * 128),

@@ -346,6 +346,7 @@ struct Ws {
   void* a[3] = {nullptr, nullptr, nullptr};
   void* u = nullptr;
   void* y = nullptr;  // GEMM outputs feeding a post-norm, model dtype
+  void* y2 = nullptr;  // bf16 models: the second output of a row-kernel pair
   void* qkv = nullptr;
   void* o = nullptr;
   void* g = nullptr;
@@ -382,6 +383,7 @@ Ws ws_layout(const ae_model* m, int B, int64_t F, int64_t T, char* base) {
   for (int i = 0; i < 3; ++i) w.a[i] = take(es * (size_t)T * d);
   w.u = take(es * (size_t)T * m->cfg.ff);
   w.y = take(es * (size_t)T * d);
+  if (m->dt == AE_BF16) w.y2 = take(es * (size_t)T * d);
   w.qkv = take(es * (size_t)T * 3 * d);
   w.o = take(es * (size_t)T * d);
   w.g = take(es * (size_t)T * d);
@@ -536,7 +538,7 @@ ae_status layer_impl(const ae_model* m, int l, float* h, const int32_t* pos, int
   const ae_layer_weights& L = Lq;
 
   auto ffn = [&](const float* pre, const void* w1, const ae_clip& c1, const void* w2,
-                 const ae_clip& c2, bool done) -> ae_status {
+                 const ae_clip& c2, bool done, void* yout) -> ae_status {
     if (!done) {
       RowNormParams r = rn_params(n, d, h);
       r.w_next = pre; r.n_out = 1; r.a[0] = w.a[0]; r.lo[0] = c1.in_lo; r.hi[0] = c1.in_hi;
@@ -546,19 +548,26 @@ ae_status layer_impl(const ae_model* m, int l, float* h, const int32_t* pos, int
     set_out_clip(p1, c1);
     p1.nlo = c2.in_lo; p1.nhi = c2.in_hi;
     AE_LAUNCH(AE_K_GEMM_FFN1, s, launch_gemm(dt, EPI_SILU, A_PLAIN, lowp, p1, s));
-    GemmParams p2 = gemm_params(w, M, d, ff, w.u, ff, w2, ff, w.y, d);
+    GemmParams p2 = gemm_params(w, M, d, ff, w.u, ff, w2, ff, yout, d);
     set_out_clip(p2, c2);
     AE_LAUNCH(AE_K_GEMM_FFN2, s, launch_gemm(dt, EPI_STORE, A_PLAIN, lowp, p2, s));
     return AE_OK;
   };
 
+  // In bf16 models the row kernels run in pairs (after FFN 1 and after the
+  // attention; after the light conv and after FFN 2): the first of a pair
+  // leaves h unwritten and the second applies both residual updates, its
+  // own GEMM output in y2 and the first's still in y.
+  void* y_second = lowp ? w.y2 : w.y;
   // ---- FFN 1
-  ae_status st = ffn(L.ff1_pre, L.ff1_w1, L.ff1_w1_clip, L.ff1_w2, L.ff1_w2_clip, pre_done);
+  ae_status st =
+      ffn(L.ff1_pre, L.ff1_w1, L.ff1_w1_clip, L.ff1_w2, L.ff1_w2_clip, pre_done, w.y);
   if (st != AE_OK) return st;
   // residual + attention pre-norm (q, k, v inputs; distinct clamps only if needed)
   {
     RowNormParams r = rn_params(n, d, h);
     r.y = w.y; r.scale = m->cfg.residual_weight; r.w_post = L.ff1_post;
+    r.skip_h = lowp;
     r.w_next = L.attn_pre;
     const ae_clip* cl[3] = {&L.q_clip, &L.k_clip, &L.v_clip};
     r.n_out = m->attn_nout[l];
@@ -589,13 +598,16 @@ ae_status layer_impl(const ae_model* m, int l, float* h, const int32_t* pos, int
                              m->cfg.heads, m->left, m->cfg.softcap, L.post_clip.in_lo,
                              L.post_clip.in_hi, w.o, s));
   {
-    GemmParams p = gemm_params(w, M, d, d, w.o, d, L.post, d, w.y, d);
+    GemmParams p = gemm_params(w, M, d, d, w.o, d, L.post, d, y_second, d);
     set_out_clip(p, L.post_clip);
     AE_LAUNCH(AE_K_GEMM_POST, s, launch_gemm(dt, EPI_STORE, A_PLAIN, lowp, p, s));
   }
   {
     RowNormParams r = rn_params(n, d, h);
-    r.y = w.y; r.scale = 1.0f; r.w_post = L.attn_post;
+    if (lowp) {
+      r.y0 = w.y; r.scale0 = m->cfg.residual_weight; r.w_post0 = L.ff1_post;
+    }
+    r.y = y_second; r.scale = 1.0f; r.w_post = L.attn_post;
     r.w_next = L.lc_pre; r.n_out = 1; r.a[0] = w.a[0];
     r.lo[0] = L.lc_start_clip.in_lo; r.hi[0] = L.lc_start_clip.in_hi;
     AE_LAUNCH(AE_K_ROWNORM, s, launch_rownorm(dt, r, s));
@@ -622,16 +634,20 @@ ae_status layer_impl(const ae_model* m, int l, float* h, const int32_t* pos, int
   {
     RowNormParams r = rn_params(n, d, h);
     r.y = w.y; r.scale = 1.0f;
+    r.skip_h = lowp;
     r.w_next = L.ff2_pre; r.n_out = 1; r.a[0] = w.a[0];
     r.lo[0] = L.ff2_w1_clip.in_lo; r.hi[0] = L.ff2_w1_clip.in_hi;
     AE_LAUNCH(AE_K_ROWNORM, s, launch_rownorm(dt, r, s));
   }
   // ---- FFN 2
-  st = ffn(L.ff2_pre, L.ff2_w1, L.ff2_w1_clip, L.ff2_w2, L.ff2_w2_clip, true);
+  st = ffn(L.ff2_pre, L.ff2_w1, L.ff2_w1_clip, L.ff2_w2, L.ff2_w2_clip, true, y_second);
   if (st != AE_OK) return st;
   {
     RowNormParams r = rn_params(n, d, h);
-    r.y = w.y; r.scale = m->cfg.residual_weight; r.w_post = L.ff2_post;
+    if (lowp) {
+      r.y0 = w.y; r.scale0 = 1.0f;  // the light conv's plain residual add
+    }
+    r.y = y_second; r.scale = m->cfg.residual_weight; r.w_post = L.ff2_post;
     r.w_out = L.norm_out;
     r.h_copy = h_copy;
     if (next) {

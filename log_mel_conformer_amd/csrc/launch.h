@@ -100,6 +100,13 @@ struct RowNormParams {
   int64_t n;
   int d;
   float* h;
+  // an earlier residual update whose h the previous launch left unwritten:
+  // applied first, the same way as the one below (a post-norm with w_post0,
+  // or a plain add when it is null)
+  const void* y0;
+  float scale0;
+  const float* w_post0;
+  bool skip_h;           // leave h unwritten (the next launch recomputes it)
   const void* y;
   float scale;
   const float* w_post;

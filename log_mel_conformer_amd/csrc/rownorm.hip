@@ -9,6 +9,12 @@
 // contiguous memory. A row is read once and every norm of the chain
 // (post-norm residual, norm_out, the next block's pre-norm and the next
 // projection's input clamp) is applied while it sits in registers.
+//
+// In bf16 models the row kernels of a layer run in pairs: the first of a
+// pair writes only the next projection's input and leaves h unwritten; the
+// second reads the h the first one read plus both GEMM outputs (bf16),
+// applies both residual updates and writes h. A pair then moves 22 bytes a
+// value where two launches that each read and write the float h move 24.
 #include "launch.h"
 
 namespace ae {
@@ -46,19 +52,22 @@ __global__ void __launch_bounds__(256) k_rownorm(RowNormParams p) {
     const float4 v = *(const float4*)(hrow + q * 256 + lane * 4);
     x[4 * q] = v.x; x[4 * q + 1] = v.y; x[4 * q + 2] = v.z; x[4 * q + 3] = v.w;
   }
-  if (p.y && !p.w_post) {
-    // a plain residual add (the light conv's linear_end output)
-    const T* yrow = (const T*)p.y + row * d;
+  // one residual update: a plain add (the light conv's linear_end output)
+  // or a post-norm add; the earlier update y0 goes through the same code as
+  // in the launch that skipped writing its h, so x comes out the same
+  auto update = [&](const void* yv, const float* w_post, float scale) {
+    const T* yrow = (const T*)yv + row * d;
+    if (!w_post) {
 #pragma unroll
-    for (int q = 0; q < NV; ++q) {
-      float y[4];
-      load4(yrow + q * 256 + lane * 4, y);
+      for (int q = 0; q < NV; ++q) {
+        float y[4];
+        load4(yrow + q * 256 + lane * 4, y);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) x[4 * q + e] += p.scale * y[e];
+        for (int e = 0; e < 4; ++e) x[4 * q + e] += scale * y[e];
+      }
+      return;
     }
-  } else if (p.y) {
     float y[VPL];
-    const T* yrow = (const T*)p.y + row * d;
     float ss = 0.f;
 #pragma unroll
     for (int q = 0; q < NV; ++q) load4(yrow + q * 256 + lane * 4, y + 4 * q);
@@ -68,11 +77,13 @@ __global__ void __launch_bounds__(256) k_rownorm(RowNormParams p) {
 #pragma unroll
     for (int q = 0; q < NV; ++q) {
       float w[4];
-      load4(p.w_post + q * 256 + lane * 4, w);
+      load4(w_post + q * 256 + lane * 4, w);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) x[4 * q + e] += p.scale * (y[4 * q + e] * inv * w[e]);
+      for (int e = 0; e < 4; ++e) x[4 * q + e] += scale * (y[4 * q + e] * inv * w[e]);
     }
-  }
+  };
+  if (p.y0) update(p.y0, p.w_post0, p.scale0);
+  if (p.y) update(p.y, p.w_post, p.scale);
   if (p.w_out) {
     float ss = 0.f;
 #pragma unroll
@@ -86,7 +97,7 @@ __global__ void __launch_bounds__(256) k_rownorm(RowNormParams p) {
       for (int e = 0; e < 4; ++e) x[4 * q + e] = x[4 * q + e] * inv * w[e];
     }
   }
-  if (p.y || p.w_out) {
+  if ((p.y || p.w_out) && !p.skip_h) {
 #pragma unroll
     for (int q = 0; q < NV; ++q)
       *(float4*)(hrow + q * 256 + lane * 4) =

@@ -77,7 +77,7 @@ def test_encoder_work_matches_independent_counts():
     conv1 total 588.0 MFLOP per token (48.23 per layer x 12, in_proj 2.10,
     out_proj 3.15, embed 1.57, conv1 2 (32 T) 32 1152 / T = 2.36), 1.411e13
     FLOP for 24000 tokens; the row kernels' bytes from a per-launch count of
-    what each one reads and writes."""
+    what each one reads and writes, in bf16 (paired launches) and in fp32."""
     cfg = types.SimpleNamespace(hidden=1024, ff=4096, out_hidden=1536, out_dim=512)
     T, F, T1, S = 24000, 32 * 2999, 32 * 1500, 32 * 480000
     pl = {"token_off": [0, T], "frame_off": [0, F], "row_off": [0, T1], "sample_off": [0, S]}
@@ -95,15 +95,24 @@ def test_encoder_work_matches_independent_counts():
     d, es = 1024, 2
     launches = [(4 + es) * d]                       # layer 0's FFN 1 pre-norm
     for layer in range(12):
-        launches += [(es + 8 + es) * d] * 3         # post FFN 1, post attention, lc add + FFN 2 pre
-        launches += [(es + 8 + es) * d]             # post FFN 2 + norm_out + next pre / bf16 copy
-    launches[-1] = (es + 8 + es) * d                # the last layer writes the head's bf16 copy
-    # FFN 2's pre-norm of each layer (h in, a out) is inside the lc add launch,
-    # and each layer's first FFN 1 pre-norm after layer 0 is inside the
-    # previous layer's last launch: 49 launches, plus the head's
+        # pairs: post FFN 1 (h, y1 in; q|k|v input out; h left unwritten),
+        # post attention (h, y1, y2 in; h, lc input out), lc add + FFN 2 pre
+        # (h, y3 in; FFN 2 input out), post FFN 2 + norm_out (h, y3, y4 in;
+        # h, next layer's input out)
+        launches += [(4 + es) * d + es * d, (4 + 2 * es) * d + (4 + es) * d] * 2
+    # the last layer's last launch writes the head's bf16 copy in place of a
+    # next input (the same bytes); FFN 2's pre-norm sits in the lc add
+    # launch and each later layer's FFN 1 pre-norm in the previous layer's
+    # last launch: 49 launches, plus the head's
     launches.append((4 + es) * 1536)
     assert len(launches) == 50
     assert abs(w["rownorm"][1] - T * sum(launches)) < 1.0
+    # float models: four launches a layer, each y and h in, h and the next
+    # input out; the last writes no next input
+    wf_rows = [(4 + 4) * d] + [(4 + 8 + 4) * d] * 48
+    wf_rows[-1] -= 4 * d
+    wf_rows.append((4 + 4) * 1536)
+    assert abs(wf["rownorm"][1] - T * sum(wf_rows)) < 1.0
     assert w["logmel"][1] == 4.0 * S + 512.0 * F
     assert w["attn"][1] == 12 * T * 4 * es * d and w["lconv"][1] == 12 * T * 2 * es * d
 
