@@ -170,13 +170,39 @@ def copy_bandwidth(torch):
     return 2.0 * COPY_PROBE_BYTES / (best / 1e3) / 1e9
 
 
+def mfma_rate(torch):
+    """The device's sustained bf16 matrix-core rate (TFLOP/s): the
+    library's probe kernel (independent matrix instructions on register
+    operands, no memory traffic; about 5 ms a run, long enough for the
+    clock to settle), best of 3, timed with events after the timed region:
+    a second denominator beside the nominal 2.5 PFLOP/s."""
+    from log_mel_conformer_amd import ae
+    sink = torch.zeros(1, dtype=torch.float32, device="cuda")
+    ae.probe_mfma(100, sink)
+    best = None
+    for _ in range(3):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        flops = ae.probe_mfma(10000, sink)
+        e1.record()
+        torch.cuda.synchronize()
+        rate = flops / (e0.elapsed_time(e1) / 1e3) / 1e12
+        best = rate if best is None else max(best, rate)
+    return best
+
+
 def add_copy_denominator(roof, torch):
     """The measured copy bandwidth, and for an HBM-bound kernel its
-    achieved bandwidth as a fraction of it."""
+    achieved bandwidth as a fraction of it; for a bf16 matrix-core kernel
+    the measured matrix-core rate and the fraction of it."""
     bw = copy_bandwidth(torch)
     roof["measured_copy_GBps"] = bw
     if roof.get("bound") == "hbm":
         roof["frac_of_copy"] = roof["achieved"] / bw
+    if roof.get("bound") == "mfma" and roof.get("peak") == PEAK_BF16_TFLOPS:
+        rate = mfma_rate(torch)
+        roof["measured_mfma_TFLOPs"] = rate
+        roof["frac_of_measured_mfma"] = roof["achieved"] / rate
     return roof
 
 

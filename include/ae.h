@@ -367,6 +367,17 @@ ae_status ae_timing_enable(int32_t cls);
  * their summed duration in milliseconds, and clear the record. */
 ae_status ae_timing_read(int64_t* launches, double* total_ms);
 
+/* Matrix-core rate probe, a measurement aid beside the timing facility:
+ * launches on stream s one kernel whose wavefronts (four 4-wavefront blocks
+ * per CU) each run `iters` rounds of eight independent bf16 32x32x16
+ * matrix instructions on register operands, with no memory traffic, and
+ * stores in *flops (host) the floating-point operations it performs; the
+ * caller times it (HIP events on s) for the device's sustained bf16 matrix
+ * rate. sink: device float, written only in a case that does not arise
+ * (it keeps the products live). iters < 1 or a null pointer:
+ * AE_ERR_INVALID. */
+ae_status ae_probe_mfma(int32_t iters, float* sink, int64_t* flops, hipStream_t s);
+
 #ifdef __cplusplus
 }
 #endif

@@ -130,6 +130,7 @@ def lib():
                                                _P, _P, _P, C.c_size_t, _P]),
             "ae_timing_enable": (C.c_int, [C.c_int32]),
             "ae_timing_read": (C.c_int, [i64p, C.POINTER(C.c_double)]),
+            "ae_probe_mfma": (C.c_int, [C.c_int32, _P, i64p, _P]),
         }
         for name, (res, args) in sigs.items():
             f = getattr(L, name)
@@ -590,3 +591,13 @@ def timing_read():
     ms = C.c_double()
     _check(lib().ae_timing_read(C.byref(n), C.byref(ms)))
     return int(n.value), float(ms.value)
+
+
+def probe_mfma(iters, sink):
+    """Launch the matrix-core rate probe on the current stream; returns the
+    flops it performs (the caller times it). sink: a CUDA float32 tensor."""
+    import torch
+    _dev(sink, "sink", torch.float32, numel=1)
+    flops = C.c_int64()
+    _check(lib().ae_probe_mfma(int(iters), _ptr(sink), C.byref(flops), _stream()))
+    return int(flops.value)
