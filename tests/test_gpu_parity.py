@@ -480,6 +480,25 @@ def test_clip_isolation_fp32():
     assert np.array_equal(alone, packed[6 * 750:])
 
 
+def test_encode_matches_layer_by_layer_bf16():
+    """ae_encode fuses each layer's FFN 1 pre-norm into the previous layer's
+    last row kernel and runs the row kernels in pairs; ae_conformer_layer
+    called once per layer on the subsampler's output gives the same bits
+    for every layer's h (two packed clips, three layers)."""
+    say("[gpu] invariant: ae_encode's layer outputs = ae_conformer_layer layer by layer, bf16")
+    W = weights(3, bf16=True)
+    m = ae.Model(W, dtype="bf16")
+    clips = [synth.multisine_clip(40, 64000), synth.pink_clip(41, 37000)]
+    wave, so = synth.pack(clips)
+    _, tr = ae.encode(m, cuda(wave), so, trace=True)
+    T = [ae.num_tokens(len(c)) for c in clips]
+    pos = cuda(np.concatenate([np.arange(t) for t in T]).astype(np.int32), torch.int32)
+    h = tr[0].clone()
+    for layer in range(3):
+        ae.conformer_layer(m, layer, h, pos)
+        assert torch.equal(h, tr[layer + 1]), layer
+
+
 def test_overlong_clip_truncated_bf16():
     """A clip past 30 s is encoded as its first 480000 samples: the 31 s
     clip, alone and packed between two short clips, gives the bits of its
