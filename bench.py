@@ -411,6 +411,8 @@ def bench_lfm2a(args, torch, ae, synth):
     launches, kms = ae.timing_read()
     ae.timing_enable(None)
     ms = (t1 - t0) * 1e3 / args.steps
+    log("[bench] the same steps without events")
+    ms_plain = time_steps(step, torch, args.steps)
     if args.copy_probe:
         copy_probe(torch)
     avg_ms = kms / max(launches, 1)
@@ -444,6 +446,7 @@ def bench_lfm2a(args, torch, ae, synth):
                      "adapter; batch 32)",
            "value": audio_s / (ms / 1e3), "unit": "audio-s/s", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+           "ms_per_step_no_events": ms_plain,
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
            "data": "synthetic (seeded waveforms, random-init weights)",
            "config": {"workload": "32 clips x 30 s multisine+noise through the LFM2A encoder: "
