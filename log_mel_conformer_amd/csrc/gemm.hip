@@ -13,11 +13,13 @@
 //
 // The epilogues fuse what follows each projection on the page: the output
 // clamp of a clippable linear, SiLU plus the next projection's input clamp
-// (feed-forward), the GLU of the light conv's linear_start, the light conv's
-// residual add, the output projection's bias, per-column q/k scaling, and
-// conv1's channel LayerNorm + ReLU; for the LFM2A encoder (cera 0.5.3,
-// audio_encoder_gpu.rs), the bias adds with ReLU, SiLU or erf GELU, the
-// GLU with its bias, and the scaled residual adds of macaron_ffn.
+// (feed-forward), the GLU of the light conv's linear_start, the output
+// projection's bias, per-column q/k scaling, and conv1's channel
+// LayerNorm + ReLU (the tower's residual adds run in the row kernels); for
+// the LFM2A encoder (cera 0.5.3, audio_encoder_gpu.rs), the bias adds with
+// ReLU, SiLU or erf GELU, the GLU with its bias, and the scaled residual
+// adds of macaron_ffn. Float operands with K = 4096 split K over four
+// blocks per tile and add the partial tiles in a second pass.
 #include <type_traits>
 
 #include "launch.h"
