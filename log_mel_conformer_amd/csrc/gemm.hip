@@ -366,6 +366,31 @@ __device__ __forceinline__ void epilogue_staged(const GemmParams& p,
       }
     }
     __syncthreads();
+    if constexpr (EPI != EPI_RESID) {
+      // the staged values are already in the output type: copy raw 16-byte
+      // chunks, consecutive lanes on consecutive bytes of a row (against
+      // 8-byte pieces widened to float and narrowed again: FFN W1 190 ->
+      // 187 us, q|k|v 143.8 -> 141.3, step 15.84 -> 15.72 ms on one box)
+      constexpr int L16 = OUTN * ES / 16;  // lanes per staged row
+      static_assert(64 % L16 == 0, "whole rows per wavefront access");
+      constexpr int RP16 = 64 / L16;
+      static_assert((R / RP16) % NW == 0, "row groups spread evenly over wavefronts");
+#pragma unroll
+      for (int t = 0; t < R / RP16 / NW; ++t) {
+        const int sr = (t * NW + wave) * RP16 + lane / L16;
+        const int cb = (lane % L16) * 16;
+        const int wr = sr / (SPI * 32), w = sr - wr * (SPI * 32);
+        const int grow = m0 + wr * WTM + (pass * SPI + w / 32) * 32 + (w & 31);
+        if (grow < p.M) {
+          // rows sit at an 8-byte pitch offset: two 8-byte LDS reads
+          const uint2 lo2 = *(const uint2*)(smem + sr * PITCH + cb);
+          const uint2 hi2 = *(const uint2*)(smem + sr * PITCH + cb + 8);
+          const uint4 v = make_uint4(lo2.x, lo2.y, hi2.x, hi2.y);
+          *(uint4*)((unsigned char*)(C + (size_t)grow * p.ldc + ocol0) + cb) = v;
+        }
+      }
+      continue;
+    }
 #pragma unroll
     for (int t = 0; t < R / RPI / NW; ++t) {
       const int sr = (t * NW + wave) * RPI + lane / LPR;
