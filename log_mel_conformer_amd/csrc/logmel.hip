@@ -258,6 +258,10 @@ __global__ void __launch_bounds__(256) k_logmel(const float* __restrict__ wave,
   int clip = -1;
   auto fo = [&](int i) -> int64_t { return lds_off ? foff[i] : frame_off[i]; };
   auto so = [&](int i) -> int64_t { return lds_off ? soff[i] : sample_off[i]; };
+  // the lane's clip kept in registers: its first frame and sample and the
+  // next clip's first frame, read again only when a frame crosses into a
+  // later clip (256 x 30 s: 358 -> 352 us against an LDS read per frame)
+  int64_t fo_cur = 0, fo_next = 0, so_cur = 0;
   // Raw samples of the frame group a block handles next: loaded one group
   // ahead (register double buffer). A frame starts 160 samples early; only
   // a clip's first frame reaches before the clip, and it (and a slot past
@@ -269,11 +273,16 @@ __global__ void __launch_bounds__(256) k_logmel(const float* __restrict__ wave,
     int64_t base = 0;
     int lim = 1 << 30;  // samples below this index are zeros (all, past the end)
     if (g < gend) {
-      if (clip < 0) clip = lds_off ? find_clip_lds(foff, B, g) : find_clip(frame_off, B, g);
-      else
-        while (fo(clip + 1) <= g) ++clip;
-      const int64_t start = so(clip);
-      base = start + (g - fo(clip)) * kHop - kHop;
+      if (clip < 0 || g >= fo_next) {
+        if (clip < 0) clip = lds_off ? find_clip_lds(foff, B, g) : find_clip(frame_off, B, g);
+        else
+          while (fo(clip + 1) <= g) ++clip;
+        fo_cur = fo(clip);
+        fo_next = fo(clip + 1);
+        so_cur = so(clip);
+      }
+      const int64_t start = so_cur;
+      base = start + (g - fo_cur) * kHop - kHop;
       lim = start > base ? (int)(start - base) : 0;
     }
     if (lim == 0) {
