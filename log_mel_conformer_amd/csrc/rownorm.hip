@@ -40,6 +40,7 @@ __device__ __forceinline__ void store4v(bf16* p, const float* v) {
 template <typename T, int VPL>
 __global__ void __launch_bounds__(256) k_rownorm(RowNormParams p) {
   constexpr int NV = VPL / 4;
+  typedef typename std::conditional<std::is_same<T, float>::value, float4, bf16x4>::type Raw;
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= p.n) return;  // uniform per wavefront
@@ -47,21 +48,37 @@ __global__ void __launch_bounds__(256) k_rownorm(RowNormParams p) {
   const float invd = 1.0f / (float)d;
   float x[VPL];
   float* hrow = p.h + row * d;
+  // every activation load of the row issued before the first use, so a
+  // wavefront waits for memory once rather than once per update (47.6 ->
+  // 45.4 us a launch on 24000 rows; loading the weight vectors up front
+  // as well gave the same time with 120 registers instead of 78)
+  Raw ra[NV], rb[NV];
+  if (p.y0) {
+#pragma unroll
+    for (int q = 0; q < NV; ++q) ra[q] = *(const Raw*)((const T*)p.y0 + row * d + q * 256 + lane * 4);
+  }
+  if (p.y) {
+#pragma unroll
+    for (int q = 0; q < NV; ++q) rb[q] = *(const Raw*)((const T*)p.y + row * d + q * 256 + lane * 4);
+  }
 #pragma unroll
   for (int q = 0; q < NV; ++q) {
     const float4 v = *(const float4*)(hrow + q * 256 + lane * 4);
     x[4 * q] = v.x; x[4 * q + 1] = v.y; x[4 * q + 2] = v.z; x[4 * q + 3] = v.w;
   }
-  // one residual update: a plain add (the light conv's linear_end output)
-  // or a post-norm add; the earlier update y0 goes through the same code as
-  // in the launch that skipped writing its h, so x comes out the same
-  auto update = [&](const void* yv, const float* w_post, float scale) {
-    const T* yrow = (const T*)yv + row * d;
+  auto widen = [&](const Raw& r, float* v) {
+    if constexpr (std::is_same<T, float>::value) {
+      v[0] = r.x; v[1] = r.y; v[2] = r.z; v[3] = r.w;
+    } else {
+      v[0] = (float)r[0]; v[1] = (float)r[1]; v[2] = (float)r[2]; v[3] = (float)r[3];
+    }
+  };
+  auto update = [&](const Raw (&raw)[NV], const float* w_post, const float* wsel, float scale) {
     if (!w_post) {
 #pragma unroll
       for (int q = 0; q < NV; ++q) {
         float y[4];
-        load4(yrow + q * 256 + lane * 4, y);
+        widen(raw[q], y);
 #pragma unroll
         for (int e = 0; e < 4; ++e) x[4 * q + e] += scale * y[e];
       }
@@ -70,7 +87,7 @@ __global__ void __launch_bounds__(256) k_rownorm(RowNormParams p) {
     float y[VPL];
     float ss = 0.f;
 #pragma unroll
-    for (int q = 0; q < NV; ++q) load4(yrow + q * 256 + lane * 4, y + 4 * q);
+    for (int q = 0; q < NV; ++q) widen(raw[q], y + 4 * q);
 #pragma unroll
     for (int i = 0; i < VPL; ++i) ss += y[i] * y[i];
     const float inv = rsqrtf(wave_sum(ss) * invd + kEps);
@@ -82,8 +99,8 @@ __global__ void __launch_bounds__(256) k_rownorm(RowNormParams p) {
       for (int e = 0; e < 4; ++e) x[4 * q + e] += scale * (y[4 * q + e] * inv * w[e]);
     }
   };
-  if (p.y0) update(p.y0, p.w_post0, p.scale0);
-  if (p.y) update(p.y, p.w_post, p.scale);
+  if (p.y0) update(ra, p.w_post0, nullptr, p.scale0);
+  if (p.y) update(rb, p.w_post, nullptr, p.scale);
   if (p.w_out) {
     float ss = 0.f;
 #pragma unroll
