@@ -1025,8 +1025,8 @@ hipError_t dispatch_f32(int epi, int aload, const GemmParams& p, hipStream_t s) 
 // epilogue.
 //  N a multiple of 1024, no residual add: 384x256, 8 wavefronts of 96x128
 //         with one fragment set, two 128-byte stages (the whole 160 KB of LDS)
-//  other N % 256 == 0, no residual add: paired 192x256 blocks, 4 wavefronts
-//         of 96x128 with one fragment set, two 64-byte stages, two blocks per CU
+//  other N % 256 == 0, no residual add: 192x128 blocks, 4 wavefronts of
+//         96x64 with one fragment set, two 64-byte stages, three blocks per CU
 //  otherwise (the fp32 residual add): 256x128, 8 wavefronts of 64x64, two
 //         blocks per CU
 template <int EPI, typename TO>
@@ -1059,8 +1059,14 @@ hipError_t run_bf16(const GemmParams& p, hipStream_t s) {
     if (p.K >= 2048) return run_dl<bf16, TO, 384, 256, 4, 2, 128, 2, EPI, 1, 8, 1>(p, s);
     return run_dl<bf16, TO, 384, 256, 4, 2, 128, 2, EPI, 1, 4, 1>(p, s);
   }
+  // outputs not a multiple of 1024 wide (the head's 1536 and 512, the
+  // LFM2A stem's 256): 192x128 blocks of four 96x64 wavefronts, three per
+  // CU. Against paired 192x256 blocks the head's projections went from
+  // 75.9 to 72.4 us on average and the LFM2A stem GEMMs from 166.0 to 128.5
+  // (out_proj's 1536 columns make 1500 such tiles, 1.95 rounds of the CUs'
+  // 768 slots, against 750 paired blocks in 1.46 rounds of 512)
   if (p.N % 256 == 0 && EPI != EPI_RESID)
-    return run_dl<bf16, TO, 192, 256, 2, 2, 64, 2, EPI, 2, 4, 1>(p, s);
+    return run_dl<bf16, TO, 192, 128, 2, 2, 64, 2, EPI, 3, 4, 1>(p, s);
   return run_dl<bf16, TO, 256, 128, 4, 2, 64, 3, EPI, 2, 2>(p, s);
 }
 
