@@ -25,10 +25,6 @@ __device__ __forceinline__ void load4(const float* p, float* v) {
   const float4 a = *(const float4*)p;
   v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
 }
-__device__ __forceinline__ void load4(const bf16* p, float* v) {
-  const bf16x4 a = *(const bf16x4*)p;
-  v[0] = (float)a[0]; v[1] = (float)a[1]; v[2] = (float)a[2]; v[3] = (float)a[3];
-}
 __device__ __forceinline__ void store4v(float* p, const float* v) {
   *(float4*)p = make_float4(v[0], v[1], v[2], v[3]);
 }
